@@ -1,0 +1,23 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+@pytest.fixture(scope="session")
+def oracle_lib():
+    """The CPU oracle, built on first use if the shared library is missing."""
+    import oracle
+    if not os.path.exists(oracle._LIB_PATH):
+        from oracle import build
+        build.build()
+    oracle.lib()
+    return oracle

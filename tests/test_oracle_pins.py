@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each test checks the oracle against something it does not compute: a library
+routine that reduces to the same mathematics (numpy's exact int64 matmul and
+its IEEE binary16 conversions), exact rational arithmetic, closed forms,
+invariants, or hand-worked fixtures under tests/golden/. Sources of each
+definition are in oracle/oracle.h.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------- helpers
+# (independent of the oracle: written against the format definition)
+
+def unpack_i4(packed: np.ndarray, K: int) -> np.ndarray:
+    """Packed signed INT4 rows -> int8 rows, with numpy bit operations."""
+    lo = (packed & 0x0F).astype(np.int16)
+    hi = (packed >> 4).astype(np.int16)
+    out = np.empty((packed.shape[0], packed.shape[1] * 2), dtype=np.int16)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    out = np.where(out >= 8, out - 16, out)
+    return out[:, :K].astype(np.int8)
+
+
+def pack_i4(q: np.ndarray) -> np.ndarray:
+    q = np.asarray(q, dtype=np.int64)
+    assert q.shape[1] % 2 == 0 and q.min() >= -8 and q.max() <= 7
+    u = (q & 0xF).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def rand_f16(r, shape, lo=-1.0, hi=1.0):
+    return r.uniform(lo, hi, size=shape).astype(np.float16)
+
+
+def read_golden(name):
+    rows = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            key, *vals = line.split()
+            rows.setdefault(key, []).append(vals)
+    return rows
+
+
+# ----------------------------------------------------------------- binary16
+
+def test_f16_decode_all_patterns_match_numpy(oracle_lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle_lib.f16_decode(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert np.signbit(oracle_lib.f16_decode(0x8000)) and not np.signbit(oracle_lib.f16_decode(0))
+
+
+def _check_encode(oracle_lib, xs):
+    xs = np.asarray(xs, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        ref = xs.astype(np.float16).view(np.uint16)
+    got = oracle_lib.f16_encode_rne_array(xs)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(xs[i], hex(got[i]), hex(ref[i])) for i in bad[:5]]
+
+
+def test_f16_encode_exact_values_and_ties(oracle_lib):
+    bits = np.arange(0, 0x7C00, dtype=np.uint16)          # all finite positives
+    v = bits.view(np.float16).astype(np.float64)
+    _check_encode(oracle_lib, np.concatenate([v, -v]))
+    # midpoints between neighbours are exact ties: round half to even
+    mid = (v[:-1] + v[1:]) / 2.0
+    _check_encode(oracle_lib, np.concatenate([mid, -mid]))
+    # just above / below each midpoint
+    _check_encode(oracle_lib, np.nextafter(mid, np.inf))
+    _check_encode(oracle_lib, np.nextafter(mid, -np.inf))
+
+
+def test_f16_encode_random_and_edges(oracle_lib):
+    r = rng(1)
+    xs = np.concatenate([
+        r.uniform(-70000, 70000, 4000),
+        r.standard_normal(4000),
+        r.standard_normal(4000) * 2.0 ** -16,               # subnormal range
+        [65504.0, 65519.99, 65520.0, 65536.0, 1e9, -65520.0, 2.0 ** -25,
+         2.0 ** -25 * 1.0000001, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 0.0, -0.0],
+    ])
+    _check_encode(oracle_lib, xs)
+    assert oracle_lib.f16_encode_rne(float("inf")) == 0x7C00
+    assert oracle_lib.f16_encode_rne(float("-inf")) == 0xFC00
+    assert (oracle_lib.f16_encode_rne(float("nan")) & 0x7C00) == 0x7C00
+
+
+# ----------------------------------------------------------------- int4 format
+
+def test_i4_nibbles_golden(oracle_lib):
+    rows = read_golden("int4_nibbles.txt")
+    assert rows
+    for key, vals in rows.items():
+        byte = int(key, 16)
+        even, odd = int(vals[0][0]), int(vals[0][1])
+        row = np.array([byte], dtype=np.uint8)
+        assert oracle_lib.i4_get(row, 0) == even, hex(byte)
+        assert oracle_lib.i4_get(row, 1) == odd, hex(byte)
+
+
+def test_i4_get_all_bytes_matches_numpy_unpack(oracle_lib):
+    row = np.arange(256, dtype=np.uint8)
+    ref = unpack_i4(row[None, :], 512)[0]
+    got = np.array([oracle_lib.i4_get(row, k) for k in range(512)])
+    assert np.array_equal(got, ref)
+
+
+# ----------------------------------------------------------------- int8 GEMM
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (4, 4, 4), (7, 13, 33), (64, 48, 100), (3, 130, 257)])
+def test_i8_matches_exact_int64_matmul(oracle_lib, M, N, K):
+    r = rng(M * 1000 + N * 10 + K)
+    A = r.integers(-128, 128, (M, K), dtype=np.int64).astype(np.int8)
+    B = r.integers(-128, 128, (N, K), dtype=np.int64).astype(np.int8)
+    ref = A.astype(np.int64) @ B.astype(np.int64).T
+    assert np.array_equal(oracle_lib.gemm_i8(A, B), ref.astype(np.int32))
+
+
+def test_i8_brute_force_4x4(oracle_lib):
+    A = np.array([[1, -2, 3, 127], [-128, 0, 5, 9], [4, 4, -4, 4], [0, 1, 0, -1]], dtype=np.int8)
+    B = np.array([[2, 3, -1, 1], [-128, 127, 0, 2], [1, 1, 1, 1], [7, -7, 7, -7]], dtype=np.int8)
+    C = oracle_lib.gemm_i8(A, B)
+    # each entry written out by hand: C[i][j] = sum_k A[i][k] * B[j][k]
+    assert C[0, 0] == 1 * 2 + (-2) * 3 + 3 * (-1) + 127 * 1
+    assert C[0, 1] == 1 * (-128) + (-2) * 127 + 3 * 0 + 127 * 2
+    assert C[1, 0] == (-128) * 2 + 0 * 3 + 5 * (-1) + 9 * 1
+    assert C[1, 1] == (-128) * (-128) + 0 * 127 + 5 * 0 + 9 * 2
+    assert C[2, 3] == 4 * 7 + 4 * (-7) + (-4) * 7 + 4 * (-7)
+    assert C[3, 2] == 0 * 1 + 1 * 1 + 0 * 1 + (-1) * 1
+    assert C[3, 3] == 0 * 7 + 1 * (-7) + 0 * 7 + (-1) * (-7)
+
+
+def test_i8_identity_and_ones(oracle_lib):
+    r = rng(7)
+    K = 37
+    A = r.integers(-128, 128, (5, K)).astype(np.int8)
+    eye = np.eye(K, dtype=np.int8)
+    assert np.array_equal(oracle_lib.gemm_i8(A, eye), A.astype(np.int32))          # B = I -> C = A
+    assert np.array_equal(oracle_lib.gemm_i8(eye, A), A.T.astype(np.int32))        # A = I -> C = B^T
+    ones_a = np.ones((3, K), dtype=np.int8)
+    C = oracle_lib.gemm_i8(ones_a, A)                                               # row sums of B
+    assert np.array_equal(C, np.tile(A.astype(np.int64).sum(1), (3, 1)))
+    full = np.full((2, 8192), -128, dtype=np.int8)
+    assert np.all(oracle_lib.gemm_i8(full, full) == 16384 * 8192)                   # 2^27
+
+
+def test_i8_overflow_is_reported(oracle_lib):
+    K = 131072                                  # 16384 * K = 2^31 leaves int32
+    full = np.full((1, K), -128, dtype=np.int8)
+    with pytest.raises(ValueError):
+        oracle_lib.gemm_i8(full, full)
+    ok = np.full((1, K - 1), -128, dtype=np.int8)
+    assert oracle_lib.gemm_i8(ok, ok)[0, 0] == 16384 * (K - 1)
+
+
+def test_i8_degenerate_shapes(oracle_lib):
+    A = np.zeros((0, 5), dtype=np.int8)
+    B = np.ones((3, 5), dtype=np.int8)
+    assert oracle_lib.gemm_i8(A, B).shape == (0, 3)
+    A0 = np.ones((2, 0), dtype=np.int8)
+    B0 = np.ones((3, 0), dtype=np.int8)
+    assert np.array_equal(oracle_lib.gemm_i8(A0, B0), np.zeros((2, 3), np.int32))   # K = 0 -> zeros
+
+
+# ----------------------------------------------------------------- int4 GEMM
+
+def test_i4_golden_worked_example(oracle_lib):
+    g = read_golden("i4_gemm_2x2x4.txt")
+    K = int(g["K"][0][0])
+    A = np.array([[int(v, 16) for v in row] for row in g["A"]], dtype=np.uint8)
+    B = np.array([[int(v, 16) for v in row] for row in g["B"]], dtype=np.uint8)
+    C = np.array([[int(v) for v in row] for row in g["C"]], dtype=np.int32)
+    assert np.array_equal(oracle_lib.gemm_i4(A, B, K), C)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 2), (4, 4, 4), (9, 5, 66), (33, 17, 258), (2, 70, 1024)])
+def test_i4_equals_i8_of_unpacked(oracle_lib, M, N, K):
+    r = rng(M + 100 * N + K)
+    Ap = r.integers(0, 256, (M, K // 2), dtype=np.int64).astype(np.uint8)
+    Bp = r.integers(0, 256, (N, K // 2), dtype=np.int64).astype(np.uint8)
+    Au, Bu = unpack_i4(Ap, K), unpack_i4(Bp, K)
+    got = oracle_lib.gemm_i4(Ap, Bp, K)
+    assert np.array_equal(got, oracle_lib.gemm_i8(Au, Bu))
+    assert np.array_equal(got, (Au.astype(np.int64) @ Bu.astype(np.int64).T).astype(np.int32))
+
+
+def test_i4_closed_forms(oracle_lib):
+    K = 8192
+    m8 = pack_i4(np.full((2, K), -8))
+    p7 = pack_i4(np.full((3, K), 7))
+    assert np.all(oracle_lib.gemm_i4(m8, m8, K) == 64 * K)
+    assert np.all(oracle_lib.gemm_i4(m8, p7, K) == -56 * K)
+    # identity: B = I (N = K) -> C = A
+    Kc = 16
+    r = rng(3)
+    q = r.integers(-8, 8, (3, Kc))
+    eye = pack_i4(np.eye(Kc, dtype=np.int64))
+    assert np.array_equal(oracle_lib.gemm_i4(pack_i4(q), eye, Kc), q.astype(np.int32))
+    # only one nibble of a byte set: catches a swapped nibble order
+    a = pack_i4(np.array([[0, 1]]))       # element k = 1 is 1
+    b = pack_i4(np.array([[5, 3]]))
+    assert oracle_lib.gemm_i4(a, b, 2)[0, 0] == 3
+
+
+def test_i4_odd_ld_rejected(oracle_lib):
+    import ctypes
+    L = oracle_lib.lib()
+    A = np.zeros((1, 2), dtype=np.uint8)
+    C = np.zeros((1, 1), dtype=np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert L.oracle_gemm_i4(1, 1, 3, p(A), 3, p(A), 4, p(C), 1) == oracle_lib.ERR_ARG
+
+
+# ----------------------------------------------------------------- fp16 GEMM
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (4, 4, 4), (6, 11, 129), (32, 40, 512), (3, 5, 8192)])
+def test_f16_matches_exact_fixed_point(oracle_lib, M, N, K):
+    """Inputs in [-1, 1] are integer multiples of 2^-24, so the exact C is an
+    integer multiple of 2^-48 and numpy's int64 matmul computes it exactly
+    (|sum| <= K * 2^48 < 2^63). The fp64 oracle must sit within the sequential
+    summation bound K * 2^-53 * sum|a b| of it."""
+    r = rng(K + 7 * M + 3 * N)
+    A = rand_f16(r, (M, K))
+    B = rand_f16(r, (N, K))
+    Ai = (A.astype(np.float64) * 2.0 ** 24).astype(np.int64)
+    Bi = (B.astype(np.float64) * 2.0 ** 24).astype(np.int64)
+    assert np.array_equal(Ai.astype(np.float64) * 2.0 ** -24, A.astype(np.float64))
+    exact = Ai @ Bi.T                                            # units of 2^-48
+    absum = np.abs(Ai) @ np.abs(Bi).T
+    got = oracle_lib.gemm_f16(A, B)
+    err = np.abs(got * 2.0 ** 48 - exact.astype(np.float64))
+    bound = K * 2.0 ** -53 * absum.astype(np.float64) + 1.0
+    assert np.all(err <= bound)
+
+
+def test_f16_small_integers_equal_int8_oracle(oracle_lib):
+    r = rng(11)
+    K = 300
+    A = r.integers(-4, 5, (9, K))
+    B = r.integers(-4, 5, (12, K))
+    got = oracle_lib.gemm_f16(A.astype(np.float16), B.astype(np.float16))
+    ref = oracle_lib.gemm_i8(A.astype(np.int8), B.astype(np.int8))
+    assert np.array_equal(got, ref.astype(np.float64))
+
+
+def test_f16_brute_force_4x4_fractions(oracle_lib):
+    r = rng(5)
+    A = rand_f16(r, (4, 4), -2, 2)
+    B = rand_f16(r, (4, 4), -2, 2)
+    got = oracle_lib.gemm_f16(A, B)
+    for i in range(4):
+        for j in range(4):
+            exact = sum(Fraction(float(A[i, k])) * Fraction(float(B[j, k])) for k in range(4))
+            assert abs(Fraction(got[i, j]) - exact) <= Fraction(1, 2 ** 45)
+
+
+def test_f16_identity_and_transpose(oracle_lib):
+    r = rng(9)
+    K = 24
+    A = rand_f16(r, (5, K), -100, 100)
+    eye = np.eye(K, dtype=np.float16)
+    assert np.array_equal(oracle_lib.gemm_f16(A, eye), A.astype(np.float64))
+    assert np.array_equal(oracle_lib.gemm_f16(eye, A), A.astype(np.float64).T)
+    # subnormal and infinite inputs take their IEEE values
+    sub = np.array([[np.float16(2.0 ** -24)]], dtype=np.float16)
+    assert oracle_lib.gemm_f16(sub, np.array([[1.0]], np.float16))[0, 0] == 2.0 ** -24
+    inf = np.array([[np.inf, 1.0]], dtype=np.float16)
+    assert oracle_lib.gemm_f16(inf, np.array([[1.0, 1.0]], np.float16))[0, 0] == np.inf
+
+
+# ----------------------------------------------------------------- W4A16
+
+def test_w4a16_golden_worked_example(oracle_lib):
+    g = read_golden("w4a16_1x1x4.txt")
+    K, G = int(g["K"][0][0]), int(g["G"][0][0])
+    X = np.array([[int(v, 16) for v in g["X"][0]]], dtype=np.uint16)
+    W = np.array([[int(v, 16) for v in g["W"][0]]], dtype=np.uint8)
+    S = np.array([[int(v, 16) for v in g["S"][0]]], dtype=np.uint16)
+    Y = oracle_lib.gemm_w4a16(X, W, S, K, G)
+    assert Y[0, 0] == float(g["Y"][0][0])
+    assert oracle_lib.f16_encode_rne(Y[0, 0]) == int(g["YBITS"][0][0], 16)
+
+
+def _w4a16_case(seed, M, N, K, G):
+    r = rng(seed)
+    X = r.standard_normal((M, K)).astype(np.float16)
+    Wp = r.integers(0, 256, (N, K // 2), dtype=np.int64).astype(np.uint8)
+    S = r.uniform(0.005, 0.02, (N, K // G)).astype(np.float16)
+    return X, Wp, S
+
+
+def test_w4a16_exact_rational_small(oracle_lib):
+    M, N, K, G = 2, 3, 16, 4
+    X, Wp, S = _w4a16_case(21, M, N, K, G)
+    q = unpack_i4(Wp, K)
+    Y, T2 = oracle_lib.gemm_w4a16(X, Wp, S, K, G, want_t2=True)
+    for m in range(M):
+        for n in range(N):
+            terms = [Fraction(float(X[m, k])) * int(q[n, k]) * Fraction(float(S[n, k // G]))
+                     for k in range(K)]
+            exact = sum(terms)
+            assert abs(Fraction(Y[m, n]) - exact) <= Fraction(1, 2 ** 40)
+            assert abs(Fraction(T2[m, n]) - sum(t * t for t in terms)) <= Fraction(1, 2 ** 40)
+
+
+def test_w4a16_one_hot_selects_group_and_nibble(oracle_lib):
+    N, K, G = 5, 64, 8
+    _, Wp, S = _w4a16_case(22, 1, N, K, G)
+    S = np.arange(1, N * (K // G) + 1, dtype=np.float64).reshape(N, K // G).astype(np.float16)
+    q = unpack_i4(Wp, K)
+    # k at group boundaries and inside groups
+    for k in [0, 1, G - 1, G, G + 1, 2 * G - 1, 2 * G, K - 1]:
+        X = np.zeros((1, K), dtype=np.float16)
+        X[0, k] = 1.0
+        Y = oracle_lib.gemm_w4a16(X, Wp, S, K, G)
+        ref = q[:, k].astype(np.float64) * S[:, k // G].astype(np.float64)
+        assert np.array_equal(Y[0], ref), k
+
+
+def test_w4a16_unit_scales_one_group_equals_f16_gemm(oracle_lib):
+    M, N, K = 3, 7, 96
+    X, Wp, _ = _w4a16_case(23, M, N, K, K)
+    S = np.ones((N, 1), dtype=np.float16)
+    q = unpack_i4(Wp, K).astype(np.float16)
+    assert np.array_equal(oracle_lib.gemm_w4a16(X, Wp, S, K, K), oracle_lib.gemm_f16(X, q))
+
+
+def test_w4a16_group_scale_closed_form(oracle_lib):
+    N, K, G = 4, 128, 32
+    X = np.ones((1, K), dtype=np.float16)
+    Wp = pack_i4(np.ones((N, K), dtype=np.int64))
+    S = (rng(24).integers(1, 64, (N, K // G)) / 64.0).astype(np.float16)
+    Y = oracle_lib.gemm_w4a16(X, Wp, S, K, G)
+    assert np.array_equal(Y[0], G * S.astype(np.float64).sum(1))
+
+
+def test_w4a16_bad_group_rejected(oracle_lib):
+    X, Wp, S = _w4a16_case(25, 1, 2, 16, 4)
+    with pytest.raises(ValueError):
+        oracle_lib.gemm_w4a16(X, Wp, S, 16, 5)           # K % G != 0
