@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""mpgemm benchmark: TFLOPS/TOPS per precision and fraction of the MI355X
+MFMA / HBM roofline, with the CPU oracle timed beside it.
+
+One step is one FP16 GEMM C = A * B^T at M = N = K = 8192 (the FP16 square
+workload at its largest size) with inputs resident in HBM; `value` is its
+throughput. The same run also measures every precision at every size of the
+workloads (FP16/INT8/INT4 square N = 512 ... 8192, W4A16 4096 x 4096 at
+M = 1, 16, 128) and one pass of the whole hot path (all of those ops at their
+largest size), reported under `per_precision` and `hot_path`.
+
+Timing: HIP events recorded on the stream the kernels are launched on (torch's
+current stream), W warm-up launches, then K timed launches between two
+synchronisations. Small problems rotate through enough distinct input copies
+that the 256 MB Infinity Cache cannot serve repeats ("cold").
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
+                       [--no-cpu-baseline] [--only f16|i8|i4|w4a16]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (no sparsity) and HBM bandwidth.
+PEAK = {"f16": 2500.0, "i8": 5000.0, "i4": 5000.0}   # TFLOP/s or TOP/s; INT4 runs on i8 MFMA
+HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+SQUARE_SIZES = [512, 1024, 2048, 4096, 8192]
+W4A16_M = [1, 16, 128]
+W4A16_NK = 4096
+W4A16_G = 128
+CONFIG_INDEX = {"i8_512": 0, "f16": 1, "i8": 2, "i4": 3, "w4a16": 4}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(prec, M, N, K, G=W4A16_G):
+    """Compulsory HBM bytes of one call: read A and B (and scales) once, write C."""
+    if prec == "f16":
+        return 2 * M * K + 2 * N * K + 4 * M * N
+    if prec == "i8":
+        return M * K + N * K + 4 * M * N
+    if prec == "i4":
+        return (M * K + N * K) // 2 + 4 * M * N
+    if prec == "w4a16":
+        return 2 * M * K + N * K // 2 + 2 * N * (K // G) + 2 * M * N
+    raise ValueError(prec)
+
+
+def roofline(prec, M, N, K, seconds):
+    ops = 2.0 * M * N * K
+    nbytes = algorithmic_bytes(prec, M, N, K)
+    if prec == "w4a16":
+        peak_ops = PEAK["f16"] * 1e12
+    else:
+        peak_ops = PEAK[prec] * 1e12
+    t_compute = ops / peak_ops
+    t_mem = nbytes / (HBM_GBS * 1e9)
+    bound = "mfma" if t_compute >= t_mem else "hbm"
+    if bound == "mfma":
+        achieved = ops / seconds / 1e12
+        peak = peak_ops / 1e12
+        unit = "TFLOP/s" if prec in ("f16", "w4a16") else "TOP/s"
+    else:
+        achieved = nbytes / seconds / 1e9
+        peak = HBM_GBS
+        unit = "GB/s"
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "algorithmic_bytes": nbytes, "ops": ops}
+
+
+# ------------------------------------------------------------------ problems
+
+class Problem:
+    """Device-resident inputs of one (precision, shape), with `copies` distinct
+    input sets when the working set would otherwise stay in the MALL."""
+
+    def __init__(self, prec, M, N, K, seed, copies=1):
+        import torch
+        from precision_dense_gemm_tiled_amd import inputs
+        self.prec, self.M, self.N, self.K = prec, M, N, K
+        if prec == "w4a16":
+            X, W, S = inputs.w4a16_problem(M, N, K, W4A16_G, seed)
+            x, w, s = (torch.from_numpy(v).cuda() for v in (X, W, S))
+            # rotate weights+scales (the streamed operand); activations stay put
+            self.ins = [(x, w.clone(), s.clone()) for _ in range(copies)]
+            self.out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        else:
+            A, B = inputs.gemm_problem(prec, M, N, K, seed)
+            a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+            self.ins = [(a, b)] + [(a.clone(), b.clone()) for _ in range(copies - 1)]
+            odt = torch.float32 if prec == "f16" else torch.int32
+            self.out = torch.empty((M, N), dtype=odt, device="cuda")
+        self.i = 0
+
+    def launch(self):
+        import precision_dense_gemm_tiled_amd as mp
+        ins = self.ins[self.i % len(self.ins)]
+        self.i += 1
+        if self.prec == "f16":
+            mp.gemm_f16(ins[0], ins[1], out=self.out)
+        elif self.prec == "i8":
+            mp.gemm_i8(ins[0], ins[1], out=self.out)
+        elif self.prec == "i4":
+            mp.gemm_i4(ins[0], ins[1], self.K, out=self.out)
+        else:
+            mp.gemm_w4a16(ins[0], ins[1], ins[2], W4A16_G, out=self.out)
+
+
+def copies_for_cold(prec, M, N, K):
+    b = algorithmic_bytes(prec, M, N, K)
+    return 1 if b >= 2 * MALL_BYTES else int(math.ceil(2 * MALL_BYTES / b))
+
+
+def time_launches(launch, steps, warmup):
+    """Average seconds per launch over `steps` launches, HIP events on the
+    current stream, synchronised on both sides of the timed region."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        launch()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3 / steps
+
+
+def sweep_entry(prec, M, N, K, seed, steps, warmup):
+    copies = copies_for_cold(prec, M, N, K)
+    p = Problem(prec, M, N, K, seed, copies)
+    # enough launches that the timed region is well above event resolution
+    est_s = max(roofline(prec, M, N, K, 1.0)["ops"] / (PEAK.get(prec, 2500.0) * 1e12 * 0.3),
+                algorithmic_bytes(prec, M, N, K) / (HBM_GBS * 1e9 * 0.3))
+    reps = int(min(max(steps, 0.05 / max(est_s, 1e-7)), 2000))
+    t = time_launches(p.launch, reps, max(warmup, 3))
+    rf = roofline(prec, M, N, K, t)
+    del p
+    import torch
+    torch.cuda.empty_cache()
+    unit = "TFLOP/s" if prec in ("f16", "w4a16") else "TOP/s"
+    return {"M": M, "N": N, "K": K, "us": round(t * 1e6, 3),
+            "throughput": round(2.0 * M * N * K / t / 1e12, 3), "unit": unit,
+            "roofline_bound": rf["bound"], "roofline_frac": rf["frac"],
+            "hbm_GBps_algorithmic": round(algorithmic_bytes(prec, M, N, K) / t / 1e9, 1),
+            "input_copies": copies, "launches": reps}
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(budget_s=12.0):
+    """The CPU oracle (test infrastructure) timed on a bounded row sample of
+    the 8192^3 FP16 problem: all of B, the first r rows of A."""
+    import oracle
+    from precision_dense_gemm_tiled_amd import inputs
+    if not os.path.exists(oracle._LIB_PATH):
+        from oracle import build
+        build.build()
+    n = 8192
+    seed = inputs.config_seed(CONFIG_INDEX["f16"], n)
+    A = inputs.f16_uniform(seed, 0, 256, n, -1.0, 1.0)
+    B = inputs.f16_uniform(seed, n * n, n, n, -1.0, 1.0)
+    rows = 4
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm_f16(A[:rows], B)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 3 or rows >= 256:
+            break
+        rows = min(256, max(rows * 2, int(rows * (budget_s / 3) / max(dt, 1e-3))))
+    value = 2.0 * rows * n * n / dt / 1e12
+    return {"value": round(value, 6), "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"FP16 8192^3 problem, first {rows} rows of A against all of B "
+                      f"({rows}x8192x8192, fp64 oracle incl. decode of B), {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["f16", "i8", "i4", "w4a16"], default=None,
+                    help="time only this precision's sweep (no headline line)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import precision_dense_gemm_tiled_amd as mp
+    from precision_dense_gemm_tiled_amd import inputs
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a gfx950 GPU")
+    mp.lib()
+    torch.cuda.set_device(0)
+
+    if args.only:
+        precs = [args.only]
+        out = {}
+        for prec in precs:
+            sizes = W4A16_M if prec == "w4a16" else SQUARE_SIZES
+            out[prec] = []
+            for s in sizes:
+                M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else (s, s, s)
+                seed = inputs.config_seed(CONFIG_INDEX[prec], s)
+                e = sweep_entry(prec, M, N, K, seed, args.steps, args.warmup)
+                log(prec, e)
+                out[prec].append(e)
+        print(json.dumps(out))
+        return
+
+    # ---- headline: FP16 8192^3, inputs resident, K timed steps
+    n = 8192
+    log(f"[bench] FP16 {n}^3: generating inputs")
+    head = Problem("f16", n, n, n, inputs.config_seed(CONFIG_INDEX["f16"], n))
+    log(f"[bench] FP16 {n}^3: {args.warmup} warm-up + {args.steps} timed steps")
+    t_step = time_launches(head.launch, args.steps, args.warmup)
+    flops = 2.0 * n * n * n
+    value = flops / t_step / 1e12
+    rf = roofline("f16", n, n, n, t_step)
+    del head
+    torch.cuda.empty_cache()
+    log(f"[bench] FP16 {n}^3: {t_step * 1e3:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    result = {
+        "metric": "TFLOPS/TOPS per precision at N=512..8192 + % of MFMA/HBM roofline",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "fp16_gemm_square_n8192", "M": n, "N": n, "K": n,
+                   "A": "fp16 U[-1,1) 8192x8192 row-major", "B": "fp16 U[-1,1) 8192x8192 stored NxK",
+                   "C": "fp32 8192x8192", "parallelism": "single_gpu"},
+        "roofline": {"bound": rf["bound"], "achieved": rf["achieved"], "peak": rf["peak"],
+                     "unit": rf["unit"], "frac": rf["frac"], "traffic": None,
+                     "kernel": "mpg::gemm_tile_kernel<f16, 256x256x64B>",
+                     "algorithmic": f"2*M*N*K = {flops:.4e} flop per launch"},
+    }
+
+    if not args.no_sweep:
+        per = {}
+        for prec in ["f16", "i8", "i4", "w4a16"]:
+            sizes = W4A16_M if prec == "w4a16" else SQUARE_SIZES
+            per[prec] = []
+            for s in sizes:
+                M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else (s, s, s)
+                idx = CONFIG_INDEX["i8_512"] if (prec == "i8" and s == 512) else CONFIG_INDEX[prec]
+                e = sweep_entry(prec, M, N, K, inputs.config_seed(idx, s), 5, 2)
+                log(f"[bench] {prec} {M}x{N}x{K}: {e['us']} us, {e['throughput']} {e['unit']}, "
+                    f"{e['roofline_bound']} frac {e['roofline_frac']}")
+                per[prec].append(e)
+        result["per_precision"] = per
+
+        # one pass of the whole hot path at the largest sizes
+        probs = [Problem(p, n, n, n, inputs.config_seed(CONFIG_INDEX[p], n)) for p in ["f16", "i8", "i4"]]
+        probs += [Problem("w4a16", m, W4A16_NK, W4A16_NK, inputs.config_seed(4, m)) for m in W4A16_M]
+
+        def hot_path():
+            for p in probs:
+                p.launch()
+        t_hp = time_launches(hot_path, 5, 1)
+        ops = sum(2.0 * p.M * p.N * p.K for p in probs)
+        result["hot_path"] = {"ops_per_pass": ops, "ms_per_pass": round(t_hp * 1e3, 4),
+                              "mixed_TOPS": round(ops / t_hp / 1e12, 3),
+                              "ops": "f16/i8/i4 8192^3 + w4a16 4096x4096 M=1,16,128"}
+        del probs
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

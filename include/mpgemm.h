@@ -1,0 +1,132 @@
+/*
+ * mpgemm.h -- multi-precision dense GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (all compute C = A * B^T with A of M x K and B of N x K, both
+ * row-major and K-contiguous, C row-major M x N, alpha = 1, beta = 0):
+ *
+ *   mpgemm_run_f16    fp16 x fp16, fp32 accumulate, fp32 C
+ *   mpgemm_run_i8     int8 x int8, int32 accumulate, int32 C (exact)
+ *   mpgemm_run_i4     signed int4 x signed int4 packed two per byte along K,
+ *                     int32 accumulate, int32 C (exact)
+ *   mpgemm_run_w4a16  fp16 activations x int4 weights with per-(row, K-group)
+ *                     fp16 scales, fp32 accumulate, fp16 Y
+ *
+ * Sources: "Hand-Written PTX Tensor-Core GEMM Kernels: A Multi-Precision Study
+ * on NVIDIA L4" (abstract and summary: the FP16 / INT8 / INT4 GEMM problem over
+ * square sizes N = 512 ... 8192) and the "fused-int4-gemm-sm75" README (project
+ * description and feature list: packed INT4 weights, sign extension, in-register
+ * dequantisation with per-group scales, group_size = 128, FP16 activations,
+ * M = 1 decode and M = 128 prefill at 4096 x 4096). The weight operand enters
+ * transposed as in Y = Q(X) Q(W)^T of "Warp-Specialized Kernel Implementation
+ * for W4A4 MatMul on Latest GPU Architectures", section 1.
+ *
+ * Common contract of every run call
+ * ---------------------------------
+ *  - Pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or retains them. Buffers must stay valid until the work
+ *    queued on `stream` has finished.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls are
+ *    asynchronous: they validate, enqueue kernels and return. A fault inside
+ *    a kernel is reported by the caller's next synchronisation, not here.
+ *  - Leading dimensions count elements of the logical type (for packed INT4:
+ *    nibbles, which must be even; the byte stride of a row is ld / 2).
+ *    Required: lda >= K, ldb >= K, ldc >= N.
+ *  - Alignment: every base pointer is 16-byte aligned and every row stride in
+ *    bytes is a multiple of 16; otherwise MPGEMM_ERR_UNSUPPORTED.
+ *  - M == 0 or N == 0 is a no-op returning MPGEMM_OK. K == 0 writes zeros.
+ *  - The library reads only the first K elements of each input row and writes
+ *    only the first N elements of each output row.
+ *  - Argument errors return before any HIP call and leave outputs untouched.
+ *  - Output rows may not overlap inputs.
+ *  - A handle is immutable after creation; calls on different streams may run
+ *    concurrently with one handle.
+ */
+#ifndef MPGEMM_H
+#define MPGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mpgemm_ctx *mpgemm_handle_t;
+
+typedef enum {
+    MPGEMM_OK = 0,
+    MPGEMM_ERR_INVALID_ARG = 1,  /* null handle/pointer, negative size, ld too small */
+    MPGEMM_ERR_UNSUPPORTED = 2,  /* alignment, odd K or ld for INT4, group size, K bound */
+    MPGEMM_ERR_DEVICE = 3,       /* no GPU, or the device is not gfx950 */
+    MPGEMM_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} mpgemm_status_t;
+
+/* Create a handle bound to `device` (device < 0: the current device). Checks
+ * that the device exists and is gfx950; caches its compute-unit count. */
+mpgemm_status_t mpgemm_create(mpgemm_handle_t *out, int device);
+
+/* Destroy a handle. NULL is accepted (no-op). */
+mpgemm_status_t mpgemm_destroy(mpgemm_handle_t h);
+
+/* Static, human-readable name of a status code. */
+const char *mpgemm_status_string(mpgemm_status_t s);
+
+/* Largest K accepted by the integer paths: every exact sum stays in int32
+ * (128 * 128 * K < 2^31 for INT8, and the INT4 kernel's 16x-scaled operands
+ * have the same bound). */
+#define MPGEMM_MAX_K_INT 131071
+
+/* FP16 GEMM ([L4 study] abstract: FP16 arithmetic).
+ * A: M x K binary16 (row stride lda), B: N x K binary16 (row stride ldb),
+ * C: M x N float (row stride ldc). C[m][n] = sum_k A[m][k] * B[n][k], every
+ * product and partial sum in fp32 (IEEE round to nearest); the summation
+ * order is unspecified. */
+mpgemm_status_t mpgemm_run_f16(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                               const uint16_t *A, int64_t lda,
+                               const uint16_t *B, int64_t ldb,
+                               float *C, int64_t ldc, void *stream);
+
+/* INT8 GEMM ([L4 study] abstract and INT8 paragraph of the summary).
+ * A: M x K int8, B: N x K int8, C: M x N int32, exact.
+ * K <= MPGEMM_MAX_K_INT, else MPGEMM_ERR_UNSUPPORTED. */
+mpgemm_status_t mpgemm_run_i8(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                              const int8_t *A, int64_t lda,
+                              const int8_t *B, int64_t ldb,
+                              int32_t *C, int64_t ldc, void *stream);
+
+/* INT4 GEMM ([L4 study] abstract and INT4 paragraph of the summary).
+ * A: M x K signed INT4 packed two per byte along K: byte k/2 of a row holds
+ * element k in its low nibble when k is even and in its high nibble when k is
+ * odd, two's complement in [-8, 7]. B: N x K, same format. C: M x N int32,
+ * exact. K, lda and ldb must be even (nibble counts); K <= MPGEMM_MAX_K_INT. */
+mpgemm_status_t mpgemm_run_i4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                              const uint8_t *A, int64_t lda,
+                              const uint8_t *B, int64_t ldb,
+                              int32_t *C, int64_t ldc, void *stream);
+
+/* Weight-only INT4 GEMM ("fused-int4-gemm-sm75" README: register
+ * dequantisation, per-group scales with group_size = 128; decode M = 1 and
+ * prefill M = 128).
+ *   Y[m][n] = fp16_rne( sum_k X[m][k] * q(n, k) * S[n][k / G] )
+ * X:  M x K binary16 activations, row stride ldx elements.
+ * Wq: N x K signed INT4 weights packed along K exactly as for mpgemm_run_i4,
+ *     row stride ldw nibbles (even).
+ * S:  N x (K / G) binary16 scales, row stride lds elements (lds >= K / G).
+ *     Symmetric quantisation: no zero point.
+ * Y:  M x N binary16 output, row stride ldy elements, rounded to nearest even
+ *     from the fp32 accumulator.
+ * G must be a power of two with 32 <= G <= K and K % G == 0. The sum is
+ * accumulated in fp32; where the scale is applied (to the fp16 weight before
+ * the product, or to the fp32 group sum after it) is unspecified.
+ * S is read as 2-byte elements and needs only 2-byte alignment (the other
+ * pointers need 16). */
+mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                 const uint16_t *X, int64_t ldx,
+                                 const uint8_t *Wq, int64_t ldw,
+                                 const uint16_t *S, int64_t lds, int64_t group_size,
+                                 uint16_t *Y, int64_t ldy, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

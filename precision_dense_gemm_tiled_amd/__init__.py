@@ -1,0 +1,225 @@
+"""Python binding of libmpgemm (include/mpgemm.h): argument marshalling only.
+
+The ``mpgemm_*`` functions mirror the C-ABI one to one (raw integer device
+pointers and a raw ``hipStream_t``). The torch-facing helpers below them only
+allocate outputs with torch, read pointers, strides and the current stream,
+and call the C-ABI; every arithmetic step runs in the HIP kernels of
+libmpgemm.so. There is no fallback: if the library is missing, or the device
+is not a gfx950, the calls raise.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "MpgemmError", "lib", "lib_path",
+    "mpgemm_create", "mpgemm_destroy", "mpgemm_status_string",
+    "mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16",
+    "Handle", "default_handle", "gemm_f16", "gemm_i8", "gemm_i4", "gemm_w4a16",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libmpgemm.so")
+
+MPGEMM_OK = 0
+MPGEMM_ERR_INVALID_ARG = 1
+MPGEMM_ERR_UNSUPPORTED = 2
+MPGEMM_ERR_DEVICE = 3
+MPGEMM_ERR_HIP = 4
+MPGEMM_MAX_K_INT = 131071
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+class MpgemmError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = int(status)
+        super().__init__(f"{what}: {mpgemm_status_string(status)} ({status})" if what
+                         else mpgemm_status_string(status))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmpgemm.so from this package directory (built in-tree)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(
+                f"{lib_path} is not built; run `python -m precision_dense_gemm_tiled_amd.build` "
+                "(hipcc, gfx950)")
+        L = ctypes.CDLL(lib_path)
+        L.mpgemm_create.argtypes = [ctypes.POINTER(_vp), ctypes.c_int]
+        L.mpgemm_create.restype = ctypes.c_int
+        L.mpgemm_destroy.argtypes = [_vp]
+        L.mpgemm_destroy.restype = ctypes.c_int
+        L.mpgemm_status_string.argtypes = [ctypes.c_int]
+        L.mpgemm_status_string.restype = ctypes.c_char_p
+        for name in ("mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4"):
+            f = getattr(L, name)
+            f.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+            f.restype = ctypes.c_int
+        L.mpgemm_run_w4a16.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
+                                       _vp, _i64, _i64, _vp, _i64, _vp]
+        L.mpgemm_run_w4a16.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------ raw C-ABI
+
+def mpgemm_status_string(status: int) -> str:
+    return lib().mpgemm_status_string(int(status)).decode()
+
+
+def mpgemm_create(device: int = -1) -> int:
+    h = _vp()
+    st = lib().mpgemm_create(ctypes.byref(h), int(device))
+    if st != MPGEMM_OK:
+        raise MpgemmError(st, "mpgemm_create")
+    return h.value
+
+
+def mpgemm_destroy(handle) -> int:
+    return lib().mpgemm_destroy(handle)
+
+
+def mpgemm_run_f16(h, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return lib().mpgemm_run_f16(h, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def mpgemm_run_i8(h, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return lib().mpgemm_run_i8(h, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def mpgemm_run_i4(h, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return lib().mpgemm_run_i4(h, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def mpgemm_run_w4a16(h, M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, stream=None) -> int:
+    return lib().mpgemm_run_w4a16(h, M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, stream)
+
+
+# ------------------------------------------------------------------ torch helpers
+
+class Handle:
+    """Owns one mpgemm handle (destroyed on close / garbage collection)."""
+
+    def __init__(self, device: int = -1):
+        self.value = mpgemm_create(device)
+
+    def close(self):
+        if self.value:
+            mpgemm_destroy(self.value)
+            self.value = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+_default = {}
+
+
+def default_handle(device=None) -> int:
+    import torch
+    dev = torch.cuda.current_device() if device is None else int(device)
+    if dev not in _default:
+        _default[dev] = Handle(dev)
+    return _default[dev].value
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _rows(t, dtype, name):
+    import torch
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name}: expected a 2-D tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if t.size(1) > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: rows must be contiguous (stride(1) == 1)")
+    return t.stride(0) if t.size(0) > 1 else max(t.size(1), 1)
+
+
+def _check(st, what):
+    if st != MPGEMM_OK:
+        raise MpgemmError(st, what)
+
+
+def gemm_f16(A, B, out=None, handle=None, stream=None):
+    """C = A @ B.T with fp16 A (M x K), B (N x K) -> fp32 C (M x N)."""
+    import torch
+    lda, ldb = _rows(A, torch.float16, "A"), _rows(B, torch.float16, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    C = torch.empty((M, N), dtype=torch.float32, device=A.device) if out is None else out
+    ldc = _rows(C, torch.float32, "C")
+    h = default_handle(A.device.index) if handle is None else handle
+    _check(mpgemm_run_f16(h, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+                          _stream(stream)), "mpgemm_run_f16")
+    return C
+
+
+def gemm_i8(A, B, out=None, handle=None, stream=None):
+    """C = A @ B.T with int8 A (M x K), B (N x K) -> int32 C (M x N), exact."""
+    import torch
+    lda, ldb = _rows(A, torch.int8, "A"), _rows(B, torch.int8, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    C = torch.empty((M, N), dtype=torch.int32, device=A.device) if out is None else out
+    ldc = _rows(C, torch.int32, "C")
+    h = default_handle(A.device.index) if handle is None else handle
+    _check(mpgemm_run_i8(h, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+                         _stream(stream)), "mpgemm_run_i8")
+    return C
+
+
+def gemm_i4(A, B, K, out=None, handle=None, stream=None):
+    """C = A @ B.T for packed signed INT4 rows (uint8 tensors, K nibbles per
+    row, low nibble = even k) -> int32 C, exact."""
+    import torch
+    lda_b, ldb_b = _rows(A, torch.uint8, "A"), _rows(B, torch.uint8, "B")
+    M, N = A.shape[0], B.shape[0]
+    C = torch.empty((M, N), dtype=torch.int32, device=A.device) if out is None else out
+    ldc = _rows(C, torch.int32, "C")
+    h = default_handle(A.device.index) if handle is None else handle
+    _check(mpgemm_run_i4(h, M, N, K, A.data_ptr(), 2 * lda_b, B.data_ptr(), 2 * ldb_b,
+                         C.data_ptr(), ldc, _stream(stream)), "mpgemm_run_i4")
+    return C
+
+
+def gemm_w4a16(X, Wq, S, group_size, out=None, handle=None, stream=None):
+    """Y = X @ dequant(Wq).T: fp16 X (M x K), packed INT4 Wq (N x K/2 uint8),
+    fp16 scales S (N x K/G) -> fp16 Y (M x N)."""
+    import torch
+    ldx = _rows(X, torch.float16, "X")
+    ldw_b = _rows(Wq, torch.uint8, "Wq")
+    lds = _rows(S, torch.float16, "S")
+    M, K = X.shape
+    N = Wq.shape[0]
+    Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    ldy = _rows(Y, torch.float16, "Y")
+    h = default_handle(X.device.index) if handle is None else handle
+    _check(mpgemm_run_w4a16(h, M, N, K, X.data_ptr(), ldx, Wq.data_ptr(), 2 * ldw_b,
+                            S.data_ptr(), lds, group_size, Y.data_ptr(), ldy, _stream(stream)),
+           "mpgemm_run_w4a16")
+    return Y

@@ -1,0 +1,229 @@
+// C-ABI of libmpgemm: handles, argument validation and kernel dispatch.
+// The public contract (argument meaning, layouts, ownership, errors) is
+// documented in include/mpgemm.h; this file enforces it before any HIP call.
+#include "mpgemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "mpgemm_internal.h"
+
+struct mpgemm_ctx {
+    int device;
+    int cu_count;
+    int forced_tile_cfg;   // -1: heuristic; else a TileCfg index (MPGEMM_TILE_CFG)
+};
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Common checks of a C = A * B^T call. elem_num/elem_den: bytes per element
+// of A and B (1/2 for packed INT4); out_bytes: bytes per element of C.
+mpgemm_status_t check_gemm(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K, const void *A,
+                           int64_t lda, const void *B, int64_t ldb, const void *C, int64_t ldc,
+                           int elem_num, int elem_den, int out_bytes, int64_t max_k, bool *noop) {
+    *noop = false;
+    if (M < 0 || N < 0 || K < 0)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return MPGEMM_OK;
+    }
+    if (!C || (K > 0 && (!A || !B)))
+        return MPGEMM_ERR_INVALID_ARG;
+    if (lda < K || ldb < K || ldc < N)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (M > INT_MAX || N > INT_MAX || K > max_k)
+        return MPGEMM_ERR_UNSUPPORTED;
+    // the tile kernel flattens the tile grid into one 32-bit dimension
+    if (((M + 63) / 64) * ((N + 63) / 64) > INT_MAX)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if ((lda * elem_num) % elem_den != 0 || (ldb * elem_num) % elem_den != 0)
+        return MPGEMM_ERR_UNSUPPORTED;
+    const int64_t lda_b = lda * elem_num / elem_den, ldb_b = ldb * elem_num / elem_den;
+    if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(C))
+        return MPGEMM_ERR_UNSUPPORTED;
+    if (lda_b % 16 != 0 || ldb_b % 16 != 0 || (ldc * out_bytes) % 16 != 0)
+        return MPGEMM_ERR_UNSUPPORTED;
+    // the handle is checked last so that every argument error above is
+    // reported without a device (and can be tested on a host without a GPU)
+    if (!h)
+        return MPGEMM_ERR_INVALID_ARG;
+    return MPGEMM_OK;
+}
+
+mpgemm_status_t bind_device(mpgemm_handle_t h) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return MPGEMM_ERR_HIP;
+    if (cur != h->device && hipSetDevice(h->device) != hipSuccess)
+        return MPGEMM_ERR_HIP;
+    return MPGEMM_OK;
+}
+
+mpgemm_status_t run_tile(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int64_t kbytes,
+                         const void *A, int64_t lda_b, const void *B, int64_t ldb_b, void *C,
+                         int64_t ldc, void *stream) {
+    mpgemm_status_t st = bind_device(h);
+    if (st != MPGEMM_OK)
+        return st;
+    mpg::GemmProblem p;
+    p.A = static_cast<const uint8_t *>(A);
+    p.B = static_cast<const uint8_t *>(B);
+    p.C = C;
+    p.lda_b = lda_b;
+    p.ldb_b = ldb_b;
+    p.ldc = ldc;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.kbytes = kbytes;
+    int cfg = h->forced_tile_cfg >= 0 ? h->forced_tile_cfg
+                                      : mpg::choose_tile_cfg(prec, M, N, kbytes, h->cu_count);
+    hipError_t e = mpg::launch_gemm(prec, cfg, p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+mpgemm_status_t mpgemm_create(mpgemm_handle_t *out, int device) {
+    if (!out)
+        return MPGEMM_ERR_INVALID_ARG;
+    *out = nullptr;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0)
+        return MPGEMM_ERR_DEVICE;
+    if (device < 0) {
+        if (hipGetDevice(&device) != hipSuccess)
+            return MPGEMM_ERR_DEVICE;
+    }
+    if (device >= count)
+        return MPGEMM_ERR_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess)
+        return MPGEMM_ERR_DEVICE;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return MPGEMM_ERR_DEVICE;
+    mpgemm_ctx *h = new (std::nothrow) mpgemm_ctx;
+    if (!h)
+        return MPGEMM_ERR_HIP;
+    h->device = device;
+    h->cu_count = prop.multiProcessorCount;
+    h->forced_tile_cfg = -1;
+    // One-parameter-at-a-time ablations: force a tile configuration by index.
+    if (const char *env = std::getenv("MPGEMM_TILE_CFG")) {
+        int v = std::atoi(env);
+        if (v >= 0 && v < mpg::CFG_COUNT)
+            h->forced_tile_cfg = v;
+    }
+    *out = h;
+    return MPGEMM_OK;
+}
+
+mpgemm_status_t mpgemm_destroy(mpgemm_handle_t h) {
+    delete h;
+    return MPGEMM_OK;
+}
+
+const char *mpgemm_status_string(mpgemm_status_t s) {
+    switch (s) {
+    case MPGEMM_OK: return "MPGEMM_OK";
+    case MPGEMM_ERR_INVALID_ARG: return "MPGEMM_ERR_INVALID_ARG";
+    case MPGEMM_ERR_UNSUPPORTED: return "MPGEMM_ERR_UNSUPPORTED";
+    case MPGEMM_ERR_DEVICE: return "MPGEMM_ERR_DEVICE";
+    case MPGEMM_ERR_HIP: return "MPGEMM_ERR_HIP";
+    default: return "MPGEMM_UNKNOWN_STATUS";
+    }
+}
+
+mpgemm_status_t mpgemm_run_f16(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                               const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                               float *C, int64_t ldc, void *stream) {
+    bool noop;
+    mpgemm_status_t st = check_gemm(h, M, N, K, A, lda, B, ldb, C, ldc, 2, 1, 4, INT64_MAX / 4, &noop);
+    if (st != MPGEMM_OK || noop)
+        return st;
+    return run_tile(h, mpg::PREC_F16, M, N, 2 * K, A, 2 * lda, B, 2 * ldb, C, ldc, stream);
+}
+
+mpgemm_status_t mpgemm_run_i8(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                              const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb,
+                              int32_t *C, int64_t ldc, void *stream) {
+    bool noop;
+    mpgemm_status_t st =
+        check_gemm(h, M, N, K, A, lda, B, ldb, C, ldc, 1, 1, 4, MPGEMM_MAX_K_INT, &noop);
+    if (st != MPGEMM_OK || noop)
+        return st;
+    return run_tile(h, mpg::PREC_I8, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+mpgemm_status_t mpgemm_run_i4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                              const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                              int32_t *C, int64_t ldc, void *stream) {
+    if (M > 0 && N > 0 && K >= 0 && ((K % 2) != 0 || (lda % 2) != 0 || (ldb % 2) != 0))
+        return MPGEMM_ERR_UNSUPPORTED;
+    bool noop;
+    mpgemm_status_t st =
+        check_gemm(h, M, N, K, A, lda, B, ldb, C, ldc, 1, 2, 4, MPGEMM_MAX_K_INT, &noop);
+    if (st != MPGEMM_OK || noop)
+        return st;
+    return run_tile(h, mpg::PREC_I4, M, N, K / 2, A, lda / 2, B, ldb / 2, C, ldc, stream);
+}
+
+mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                 const uint16_t *X, int64_t ldx, const uint8_t *Wq, int64_t ldw,
+                                 const uint16_t *S, int64_t lds, int64_t group_size,
+                                 uint16_t *Y, int64_t ldy, void *stream) {
+    if (M < 0 || N < 0 || K < 0)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0)
+        return MPGEMM_OK;
+    if (!Y || (K > 0 && (!X || !Wq || !S)))
+        return MPGEMM_ERR_INVALID_ARG;
+    if (ldx < K || ldw < K || ldy < N)
+        return MPGEMM_ERR_INVALID_ARG;
+    const bool pow2 = group_size > 0 && (group_size & (group_size - 1)) == 0;
+    if (K > 0) {
+        if (!pow2 || group_size < 32 || group_size > K || K % group_size != 0)
+            return MPGEMM_ERR_UNSUPPORTED;
+        if (lds < K / group_size)
+            return MPGEMM_ERR_INVALID_ARG;
+    }
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX || (M + 31) / 32 > 65535)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if ((ldw % 2) != 0)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if ((K > 0 && (!aligned16(X) || !aligned16(Wq) || (reinterpret_cast<uintptr_t>(S) & 1u))) ||
+        !aligned16(Y))
+        return MPGEMM_ERR_UNSUPPORTED;
+    if ((ldx * 2) % 16 != 0 || (ldw / 2) % 16 != 0 || (ldy * 2) % 16 != 0)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if (!h)
+        return MPGEMM_ERR_INVALID_ARG;
+    mpgemm_status_t st = bind_device(h);
+    if (st != MPGEMM_OK)
+        return st;
+    mpg::W4A16Problem p;
+    p.X = X;
+    p.W = Wq;
+    p.S = S;
+    p.Y = Y;
+    p.ldx = ldx;
+    p.ldw_b = ldw / 2;
+    p.lds = lds;
+    p.ldy = ldy;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.G = K > 0 ? (int)group_size : 32;
+    hipError_t e = mpg::launch_w4a16(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
+}
+
+}  // extern "C"

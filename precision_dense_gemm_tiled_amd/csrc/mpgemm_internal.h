@@ -1,0 +1,50 @@
+// Internal interface between the C-ABI layer (api.cpp) and the gfx950 kernels.
+// Arguments reaching these launchers have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mpg {
+
+enum Prec { PREC_F16 = 0, PREC_I8 = 1, PREC_I4 = 2 };
+
+// One dense GEMM C = A * B^T, described in bytes of the packed K dimension:
+// kbytes = 2K (f16), K (i8) or K/2 (i4). Row strides are in bytes for A and B
+// and in output elements for C.
+struct GemmProblem {
+    const uint8_t *A;
+    const uint8_t *B;
+    void *C;
+    int64_t lda_b, ldb_b, ldc;
+    int M, N;
+    int64_t kbytes;
+};
+
+// Tile configurations of the square/rectangular tile kernel. The index is
+// stable (it names the configuration in profiles and the ablation override).
+enum TileCfg {
+    CFG_256x256 = 0,   // 4 waves of 128x128, BK = 64 B
+    CFG_128x128 = 1,   // 4 waves of 64x64,  BK = 64 B
+    CFG_64x64 = 2,     // 4 waves of 32x32,  BK = 128 B
+    CFG_256x128 = 3,   // 4 waves of 128x64, BK = 64 B
+    CFG_COUNT
+};
+
+const char *tile_cfg_name(int cfg);
+int choose_tile_cfg(int prec, int64_t M, int64_t N, int64_t kbytes, int cu_count);
+hipError_t launch_gemm(int prec, int cfg, const GemmProblem &p, hipStream_t stream);
+
+// Weight-only INT4 GEMM Y = X * dequant(Wq)^T.
+struct W4A16Problem {
+    const uint16_t *X;   // M x K fp16
+    const uint8_t *W;    // N x K packed int4
+    const uint16_t *S;   // N x K/G fp16 scales
+    uint16_t *Y;         // M x N fp16
+    int64_t ldx, ldw_b, lds, ldy;
+    int M, N, K, G;
+};
+
+hipError_t launch_w4a16(const W4A16Problem &p, hipStream_t stream);
+
+}  // namespace mpg

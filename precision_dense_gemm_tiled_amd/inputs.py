@@ -26,36 +26,57 @@ import numpy as np
 GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
+# shift counts as 0-d arrays: numpy shifts by a numpy scalar far more slowly
+_S11, _S27, _S30, _S31, _S56 = (np.array(v, dtype=np.uint64) for v in (11, 27, 30, 31, 56))
 _CHUNK = 1 << 22
+
+
+def _chunks(seed: int, start: int, count: int):
+    """Yield (offset, draws) for draws start .. start+count-1 in chunks; the
+    yielded array is reused by the next iteration."""
+    s = np.array(seed & 0xFFFFFFFFFFFFFFFF, dtype=np.uint64)
+    step = min(_CHUNK, max(count, 1))
+    z = np.empty(step, dtype=np.uint64)
+    t = np.empty(step, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        for c0 in range(0, count, _CHUNK):
+            n = min(_CHUNK, count - c0)
+            zz, tt = z[:n], t[:n]
+            # counter i + 1 (an int64 arange is much faster than a uint64 one)
+            zz.view(np.int64)[:] = np.arange(start + c0 + 1, start + c0 + 1 + n, dtype=np.int64)
+            zz *= GOLDEN
+            zz += s
+            for mult, sh in ((_M1, _S30), (_M2, _S27)):
+                np.right_shift(zz, sh, out=tt)
+                zz ^= tt
+                zz *= mult
+            np.right_shift(zz, _S31, out=tt)
+            zz ^= tt
+            yield c0, zz
 
 
 def splitmix64(seed: int, start: int, count: int) -> np.ndarray:
     """Draws start .. start+count-1 of the SplitMix64 stream with this seed."""
     out = np.empty(count, dtype=np.uint64)
-    s = np.uint64(seed & 0xFFFFFFFFFFFFFFFF)
-    with np.errstate(over="ignore"):
-        for c0 in range(0, count, _CHUNK):
-            n = min(_CHUNK, count - c0)
-            z = np.arange(start + c0 + 1, start + c0 + 1 + n, dtype=np.uint64)
-            z *= GOLDEN
-            z += s
-            z ^= z >> np.uint64(30)
-            z *= _M1
-            z ^= z >> np.uint64(27)
-            z *= _M2
-            z ^= z >> np.uint64(31)
-            out[c0:c0 + n] = z
+    for c0, z in _chunks(seed, start, count):
+        out[c0:c0 + z.size] = z
     return out
 
 
 def _top_byte(seed, start, count):
-    return (splitmix64(seed, start, count) >> np.uint64(56)).astype(np.uint8)
+    out = np.empty(count, dtype=np.uint8)
+    for c0, z in _chunks(seed, start, count):
+        out[c0:c0 + z.size] = z >> _S56
+    return out
 
 
-def _unit(seed, start, count):
-    """Uniform doubles in [0, 1) with 53 random bits."""
-    r = splitmix64(seed, start, count)
-    return (r >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+def _unit_to_f16(seed, start, count, lo, hi):
+    """lo + (hi - lo) * u, u uniform in [0, 1) with 53 bits, rounded to fp16."""
+    out = np.empty(count, dtype=np.float16)
+    for c0, z in _chunks(seed, start, count):
+        u = (z >> _S11).view(np.int64).astype(np.float64) * (2.0 ** -53)
+        out[c0:c0 + z.size] = lo + (hi - lo) * u
+    return out
 
 
 def int8_uniform(seed: int, start: int, rows: int, cols: int) -> np.ndarray:
@@ -73,15 +94,14 @@ def int4_packed_uniform(seed: int, start: int, rows: int, k: int) -> np.ndarray:
 
 
 def f16_uniform(seed: int, start: int, rows: int, cols: int, lo: float, hi: float) -> np.ndarray:
-    u = _unit(seed, start, rows * cols)
-    return (lo + (hi - lo) * u).astype(np.float16).reshape(rows, cols)
+    return _unit_to_f16(seed, start, rows * cols, lo, hi).reshape(rows, cols)
 
 
 def f16_normal(seed: int, start: int, rows: int, cols: int) -> np.ndarray:
     n = rows * cols
     r = splitmix64(seed, start, 2 * n)
-    u1 = ((r[0::2] >> np.uint64(11)).astype(np.float64) + 1.0) * (2.0 ** -53)   # (0, 1]
-    u2 = (r[1::2] >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)           # [0, 1)
+    u1 = ((r[0::2] >> _S11).view(np.int64).astype(np.float64) + 1.0) * (2.0 ** -53)   # (0, 1]
+    u2 = (r[1::2] >> _S11).view(np.int64).astype(np.float64) * (2.0 ** -53)           # [0, 1)
     z = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * math.pi * u2)
     return z.astype(np.float16).reshape(rows, cols)
 

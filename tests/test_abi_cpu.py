@@ -1,0 +1,113 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol
+include/mpgemm.h declares, and reports argument errors before any device
+work (the handle is checked last, so a NULL handle reaches every check)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpgemm.h")
+
+
+@pytest.fixture(scope="module")
+def mp():
+    import precision_dense_gemm_tiled_amd as mp
+    if not os.path.exists(mp.lib_path):
+        from precision_dense_gemm_tiled_amd import build
+        build.build()
+    mp.lib()
+    return mp
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mpgemm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_symbols()
+    for n in ["mpgemm_create", "mpgemm_destroy", "mpgemm_status_string", "mpgemm_run_f16",
+              "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(mp):
+    L = mp.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(mp):
+    assert mp.mpgemm_status_string(0) == "MPGEMM_OK"
+    assert mp.mpgemm_status_string(2) == "MPGEMM_ERR_UNSUPPORTED"
+    assert mp.mpgemm_status_string(3) == "MPGEMM_ERR_DEVICE"
+    assert mp.mpgemm_status_string(99) == "MPGEMM_UNKNOWN_STATUS"
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present")
+def test_create_without_gpu_reports_device_error(mp):
+    h = ctypes.c_void_p()
+    assert mp.lib().mpgemm_create(ctypes.byref(h), -1) == mp.MPGEMM_ERR_DEVICE
+    assert h.value is None
+    with pytest.raises(mp.MpgemmError):
+        mp.mpgemm_create()
+
+
+def test_destroy_null_is_ok(mp):
+    assert mp.mpgemm_destroy(None) == 0
+    assert mp.lib().mpgemm_create(None, 0) == mp.MPGEMM_ERR_INVALID_ARG
+
+
+# fake, never dereferenced device addresses (16-byte aligned)
+A, B, C, S = 0x10000, 0x20000, 0x30000, 0x40000
+
+
+@pytest.mark.parametrize("call,expect", [
+    # sizes
+    (("i8", -1, 4, 4, A, 16, B, 16, C, 16), 1),
+    (("i8", 4, 4, -2, A, 16, B, 16, C, 16), 1),
+    # zero-sized problems are no-ops
+    (("i8", 0, 4, 4, 0, 16, 0, 16, 0, 16), 0),
+    (("f16", 4, 0, 4, 0, 16, 0, 16, 0, 16), 0),
+    # pointers
+    (("i8", 4, 4, 16, 0, 16, B, 16, C, 16), 1),
+    (("i8", 4, 4, 16, A, 16, B, 16, 0, 16), 1),
+    # leading dimensions
+    (("i8", 4, 4, 32, A, 16, B, 32, C, 16), 1),
+    (("f16", 4, 8, 16, A, 16, B, 16, C, 4), 1),
+    # alignment of pointers and row strides
+    (("i8", 4, 4, 16, A + 4, 16, B, 16, C, 16), 2),
+    (("i8", 4, 4, 16, A, 24, B, 16, C, 16), 2),
+    (("f16", 4, 4, 16, A, 20, B, 16, C, 16), 2),
+    (("f16", 4, 6, 16, A, 16, B, 16, C, 6), 2),
+    # INT4: odd K or odd ld
+    (("i4", 4, 4, 31, A, 32, B, 32, C, 16), 2),
+    (("i4", 4, 4, 32, A, 33, B, 32, C, 16), 2),
+    # integer K bound (exact int32 results)
+    (("i8", 4, 4, 131072, A, 131072, B, 131072, C, 16), 2),
+    (("i4", 4, 4, 131072, A, 131072, B, 131072, C, 16), 2),
+    # everything valid: only the NULL handle is left to report
+    (("i8", 4, 4, 16, A, 16, B, 16, C, 16), 1),
+])
+def test_gemm_argument_errors_without_device(mp, call, expect):
+    prec, *args = call
+    f = {"i8": mp.mpgemm_run_i8, "i4": mp.mpgemm_run_i4, "f16": mp.mpgemm_run_f16}[prec]
+    assert f(None, *args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((1, 16, 256, A, 256, B, 256, S, 2, 128, C, 16), 1),     # valid: NULL handle
+    ((1, 16, 256, A, 256, B, 256, S, 2, 100, C, 16), 2),     # G not a power of two
+    ((1, 16, 256, A, 256, B, 256, S, 16, 16, C, 16), 2),     # G below 32
+    ((1, 16, 192, A, 256, B, 256, S, 2, 128, C, 16), 2),     # K % G != 0
+    ((1, 16, 256, A, 256, B, 256, S, 1, 128, C, 16), 1),     # lds < K/G
+    ((1, 16, 256, A, 256, B, 256, S + 1, 2, 128, C, 16), 2),  # scales not 2-byte aligned
+    ((1, 16, 256, A, 256, B, 250, S, 2, 128, C, 16), 1),     # ldw < K
+    ((1, 16, 256, A, 260, B, 256, S, 2, 128, C, 16), 2),     # X row stride not 16 B
+    ((0, 16, 256, 0, 256, 0, 256, 0, 2, 128, 0, 16), 0),     # M = 0: no-op
+])
+def test_w4a16_argument_errors_without_device(mp, args, expect):
+    assert mp.mpgemm_run_w4a16(None, *args, None) == expect

@@ -1,0 +1,294 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle.
+
+Integer paths must match bit for bit; FP16 within 2^-10 * sqrt(K) per element
+(fp32 output against the fp64 oracle); W4A16 within the bar in gpu_util.
+Small and ragged shapes are compared element by element; the full workload
+sizes compare sampled rows against the oracle plus an exact Freivalds check
+of every element (integer paths).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import precision_dense_gemm_tiled_amd as mp
+from precision_dense_gemm_tiled_amd import inputs
+from tests.gpu_util import (dev, f16_tol, freivalds_int, host, pack_i4, require_gpu,
+                            sample_rows, unpack_i4, w4a16_tol)
+
+pytestmark = pytest.mark.gpu
+
+SMALL_SHAPES = [(1, 1, 2), (1, 1, 64), (2, 3, 16), (7, 13, 34), (64, 64, 64), (100, 200, 300),
+                (256, 256, 512), (257, 129, 1000), (513, 300, 64), (33, 700, 130), (1, 517, 258)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu(oracle_lib):
+    require_gpu()
+    return True
+
+
+def _run(prec, A, B, K):
+    if prec == "i8":
+        return host(mp.gemm_i8(dev(A), dev(B)))
+    if prec == "i4":
+        return host(mp.gemm_i4(dev(A), dev(B), K))
+    return host(mp.gemm_f16(dev(A), dev(B)))
+
+
+def _ref(prec, A, B, K):
+    if prec == "i8":
+        return oracle.gemm_i8(A, B)
+    if prec == "i4":
+        return oracle.gemm_i4(A, B, K)
+    return oracle.gemm_f16(A, B)
+
+
+def _compare(prec, got, ref, K, what):
+    if prec == "f16":
+        err = np.abs(got.astype(np.float64) - ref)
+        assert np.all(err <= f16_tol(K)), f"{what}: max err {err.max()} > {f16_tol(K)}"
+    else:
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"{what}: {len(bad)} mismatches, first {bad[:4].tolist()}"
+
+
+# ------------------------------------------------------------------ small shapes
+
+@pytest.mark.parametrize("prec", ["i8", "i4", "f16"])
+@pytest.mark.parametrize("M,N,K", SMALL_SHAPES)
+def test_small_shapes(prec, M, N, K):
+    A, B = inputs.gemm_problem(prec, M, N, K, seed=M * 131 + N * 7 + K)
+    got = _run(prec, A, B, K)
+    _compare(prec, got, _ref(prec, A, B, K), K, f"{prec} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("prec", ["i8", "i4", "f16"])
+def test_every_tile_config(prec, monkeypatch):
+    """Each tile configuration (forced through the ablation override) on a
+    ragged shape spanning several tiles."""
+    M, N, K = 300, 520, 200
+    A, B = inputs.gemm_problem(prec, M, N, K, seed=77)
+    ref = _ref(prec, A, B, K)
+    for cfg in range(4):
+        monkeypatch.setenv("MPGEMM_TILE_CFG", str(cfg))
+        with mp.Handle() as h:
+            a, b = dev(A), dev(B)
+            if prec == "i8":
+                got = host(mp.gemm_i8(a, b, handle=h.value))
+            elif prec == "i4":
+                got = host(mp.gemm_i4(a, b, K, handle=h.value))
+            else:
+                got = host(mp.gemm_f16(a, b, handle=h.value))
+        _compare(prec, got, ref, K, f"{prec} cfg {cfg}")
+
+
+def test_i4_equals_i8_of_unpacked_on_gpu():
+    M, N, K = 190, 260, 384
+    Ap, Bp = inputs.gemm_problem("i4", M, N, K, seed=4242)
+    c4 = _run("i4", Ap, Bp, K)
+    c8 = _run("i8", unpack_i4(Ap, K), unpack_i4(Bp, K), K)
+    assert np.array_equal(c4, c8)
+
+
+def test_i4_extremes():
+    K = 4096
+    m8 = pack_i4(np.full((40, K), -8))
+    p7 = pack_i4(np.full((70, K), 7))
+    assert np.all(_run("i4", m8, m8, K) == 64 * K)
+    assert np.all(_run("i4", m8, p7, K) == -56 * K)
+
+
+def test_i8_extremes():
+    K = 8192
+    full = np.full((64, K), -128, dtype=np.int8)
+    assert np.all(_run("i8", full, full, K) == 16384 * K)
+    top = np.full((64, K), 127, dtype=np.int8)
+    assert np.all(_run("i8", full, top, K) == -128 * 127 * K)
+
+
+def test_f16_small_integers_bit_exact():
+    """Integers in [-4, 4]: every partial sum is an integer below 2^24, so an
+    fp32 accumulator is exact in any order and C must equal the INT8 oracle."""
+    r = np.random.default_rng(5)
+    M, N, K = 130, 200, 2048
+    A = r.integers(-4, 5, (M, K))
+    B = r.integers(-4, 5, (N, K))
+    got = _run("f16", A.astype(np.float16), B.astype(np.float16), K)
+    ref = oracle.gemm_i8(A.astype(np.int8), B.astype(np.int8))
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
+def test_strided_operands_and_output():
+    import torch
+    M, N, K = 70, 90, 100
+    for prec in ["i8", "f16", "i4"]:
+        A, B = inputs.gemm_problem(prec, M, N, K, seed=9)
+        pad = 64 if prec != "i4" else 32
+        Ab = np.zeros((M, A.shape[1] + pad), dtype=A.dtype)
+        Bb = np.zeros((N, B.shape[1] + pad), dtype=B.dtype)
+        Ab[:, :A.shape[1]] = A
+        Bb[:, :B.shape[1]] = B
+        # garbage in the padding must not leak into C
+        Ab[:, A.shape[1]:] = np.array(0x77, dtype=np.uint8).view(A.dtype) if A.dtype != np.float16 else np.float16(np.nan)
+        Bb[:, B.shape[1]:] = np.array(0x77, dtype=np.uint8).view(B.dtype) if B.dtype != np.float16 else np.float16(np.nan)
+        a = dev(Ab)[:, :A.shape[1]]
+        b = dev(Bb)[:, :B.shape[1]]
+        cdt = torch.float32 if prec == "f16" else torch.int32
+        cbig = torch.full((M, N + 12), -1, dtype=cdt, device="cuda")
+        c = cbig[:, :N]
+        if prec == "i8":
+            mp.gemm_i8(a, b, out=c)
+        elif prec == "i4":
+            mp.gemm_i4(a, b, K, out=c)
+        else:
+            mp.gemm_f16(a, b, out=c)
+        whole = host(cbig)
+        _compare(prec, whole[:, :N], _ref(prec, A, B, K), K, f"{prec} strided")
+        assert np.all(whole[:, N:] == -1), "wrote past N"
+
+
+def test_k_zero_writes_zeros():
+    import torch
+    h = mp.default_handle()
+    a = torch.zeros((8, 16), dtype=torch.int8, device="cuda")
+    c = torch.full((8, 8), 5, dtype=torch.int32, device="cuda")
+    st = mp.mpgemm_run_i8(h, 8, 8, 0, a.data_ptr(), 16, a.data_ptr(), 16, c.data_ptr(), 8,
+                          torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    assert np.all(host(c) == 0)
+
+
+# ------------------------------------------------------------------ workload sizes
+
+def _full_size(prec, cfg_index, n):
+    A, B = inputs.gemm_problem(prec, n, n, n, inputs.config_seed(cfg_index, n))
+    got = _run(prec, A, B, n)
+    if n <= 2048:
+        _compare(prec, got, _ref(prec, A, B, n), n, f"{prec} N={n}")
+        return
+    rows = sample_rows(n, 24, seed=n)
+    ref_rows = _ref(prec, np.ascontiguousarray(A[rows]), B, n)
+    _compare(prec, got[rows], ref_rows, n, f"{prec} N={n} sampled rows")
+    if prec == "i8":
+        freivalds_int(got, A, B, seed=n)
+    elif prec == "i4":
+        freivalds_int(got, unpack_i4(A, n), unpack_i4(B, n), seed=n)
+    else:
+        r = np.random.default_rng(n).choice([-1.0, 1.0], size=n)
+        lhs = got.astype(np.float64) @ r
+        rhs = A.astype(np.float64) @ (B.astype(np.float64).T @ r)
+        assert np.all(np.abs(lhs - rhs) <= n * f16_tol(n)), "f16 Freivalds bound"
+
+
+def test_int8_512_config0():
+    _full_size("i8", 0, 512)
+
+
+@pytest.mark.parametrize("n", [512, 1024, 2048, 4096, 8192])
+def test_fp16_square_config1(n):
+    _full_size("f16", 1, n)
+
+
+@pytest.mark.parametrize("n", [1024, 2048, 4096, 8192])
+def test_int8_square_config2(n):
+    _full_size("i8", 2, n)
+
+
+@pytest.mark.parametrize("n", [512, 1024, 2048, 4096, 8192])
+def test_int4_square_config3(n):
+    _full_size("i4", 3, n)
+
+
+# ------------------------------------------------------------------ W4A16
+
+def _w4(X, W, S, G):
+    return host(mp.gemm_w4a16(dev(X), dev(W), dev(S), G)).view(np.uint16)
+
+
+def _check_w4(X, W, S, K, G, what):
+    got = _w4(X, W, S, G).view(np.float16).astype(np.float64)
+    y, t2 = oracle.gemm_w4a16(X, W, S, K, G, want_t2=True)
+    err = np.abs(got - y)
+    tol = w4a16_tol(y, t2, K)
+    bad = np.argwhere(err > tol)
+    assert bad.size == 0, f"{what}: {len(bad)} outside the bar, worst {err.max()}"
+
+
+@pytest.mark.parametrize("M", [1, 16, 128])
+def test_w4a16_config4(M):
+    N = K = 4096
+    G = 128
+    X, W, S = inputs.w4a16_problem(M, N, K, G, inputs.config_seed(4, M))
+    _check_w4(X, W, S, K, G, f"w4a16 M={M}")
+
+
+@pytest.mark.parametrize("M,N,K,G", [(1, 16, 128, 128), (3, 50, 256, 128), (17, 70, 512, 128),
+                                     (5, 33, 96, 32), (40, 130, 192, 64), (200, 64, 1024, 256),
+                                     (2, 300, 4096, 4096)])
+def test_w4a16_ragged(M, N, K, G):
+    X, W, S = inputs.w4a16_problem(M, N, K, G, seed=M * 1000 + N + K + G)
+    _check_w4(X, W, S, K, G, f"w4a16 {M}x{N}x{K} G={G}")
+
+
+@pytest.mark.parametrize("G", [32, 128])
+def test_w4a16_one_hot_exact(G):
+    """x = e_k: y[n] = rne16(q[n,k] * s[n, k/G]) exactly (a single nonzero term)."""
+    N, K = 48, 512
+    _, W, S = inputs.w4a16_problem(1, N, K, G, seed=31)
+    q = unpack_i4(W, K)
+    ks = [0, 1, 7, 8, G - 1, G, G + 1, K - 1]
+    X = np.zeros((len(ks), K), dtype=np.float16)
+    for i, k in enumerate(ks):
+        X[i, k] = 1.0
+    got = _w4(X, W, S, G)
+    for i, k in enumerate(ks):
+        exact = q[:, k].astype(np.float64) * S[:, k // G].astype(np.float64)
+        assert np.array_equal(got[i], oracle.f16_encode_rne_array(exact)), f"k={k}"
+
+
+@pytest.mark.parametrize("M,G", [(1, 128), (16, 128), (128, 128), (16, 64)])
+def test_w4a16_exact_small_integers(M, G):
+    """Small-integer x and power-of-two scales: every partial sum is exact in
+    fp32, so Y must be the fp16 rounding of the exact sum, bit for bit."""
+    N, K = 256, 4096
+    r = np.random.default_rng(M + G)
+    X = r.integers(-4, 5, (M, K)).astype(np.float16)
+    W = r.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    S = (2.0 ** -r.integers(3, 9, (N, K // G))).astype(np.float16)
+    y = oracle.gemm_w4a16(X, W, S, K, G)
+    assert np.array_equal(_w4(X, W, S, G), oracle.f16_encode_rne_array(y))
+
+
+def test_w4a16_strided():
+    import torch
+    M, N, K, G = 9, 40, 256, 128
+    X, W, S = inputs.w4a16_problem(M, N, K, G, seed=3)
+    Xb = np.zeros((M, K + 64), np.float16); Xb[:, :K] = X; Xb[:, K:] = np.nan
+    Wb = np.full((N, K // 2 + 32), 0x88, np.uint8); Wb[:, :K // 2] = W
+    Sb = np.full((N, K // G + 5), np.nan, np.float16); Sb[:, :K // G] = S
+    ybig = torch.full((M, N + 8), -7.0, dtype=torch.float16, device="cuda")
+    mp.gemm_w4a16(dev(Xb)[:, :K], dev(Wb)[:, :K // 2], dev(Sb)[:, :K // G], G, out=ybig[:, :N])
+    whole = host(ybig)
+    y, t2 = oracle.gemm_w4a16(X, W, S, K, G, want_t2=True)
+    assert np.all(np.abs(whole[:, :N].astype(np.float64) - y) <= w4a16_tol(y, t2, K))
+    assert np.all(whole[:, N:] == -7.0)
+
+
+# ------------------------------------------------------------------ argument errors with a device
+
+def test_argument_errors_with_handle():
+    import torch
+    h = mp.default_handle()
+    a = torch.zeros((64, 64), dtype=torch.int8, device="cuda")
+    c = torch.zeros((64, 64), dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    A, C = a.data_ptr(), c.data_ptr()
+    assert mp.mpgemm_run_i8(h, 64, 64, 64, A + 1, 64, A, 64, C, 64, s) == mp.MPGEMM_ERR_UNSUPPORTED
+    assert mp.mpgemm_run_i8(h, 64, 64, 64, A, 63, A, 64, C, 64, s) == mp.MPGEMM_ERR_INVALID_ARG
+    assert mp.mpgemm_run_i8(h, 64, 64, 64, A, 72, A, 64, C, 64, s) == mp.MPGEMM_ERR_UNSUPPORTED
+    assert mp.mpgemm_run_i4(h, 64, 64, 63, A, 64, A, 64, C, 64, s) == mp.MPGEMM_ERR_UNSUPPORTED
+    assert mp.mpgemm_run_i8(h, 64, 64, 200000, A, 200000, A, 200000, C, 64, s) == mp.MPGEMM_ERR_UNSUPPORTED
+    assert mp.mpgemm_run_w4a16(h, 1, 64, 64, A, 64, A, 64, A, 1, 48, C, 64, s) == mp.MPGEMM_ERR_UNSUPPORTED
+    assert mp.mpgemm_run_i8(h, 0, 64, 64, 0, 64, 0, 64, 0, 64, s) == mp.MPGEMM_OK
+    torch.cuda.synchronize()
+    assert np.all(host(c) == 0), "an argument error touched the output"
