@@ -31,11 +31,17 @@
  *  - Leading dimensions count elements of the logical type (for packed INT4:
  *    nibbles, which must be even; the byte stride of a row is ld / 2).
  *    Required: lda >= K, ldb >= K, ldc >= N.
- *  - Alignment: every base pointer is 16-byte aligned and every row stride in
- *    bytes is a multiple of 16; otherwise MPGEMM_ERR_UNSUPPORTED.
+ *  - Alignment: outputs need only the alignment of their element type. For
+ *    mpgemm_run_{f16,i8,i4}, A and B may have any alignment, but rows that are
+ *    16-byte aligned (base pointer and row stride in bytes) take the fast
+ *    kernel; other rows are read with byte gathers. mpgemm_run_w4a16 requires
+ *    X and Wq 16-byte aligned with row strides that are multiples of 16 bytes
+ *    (else MPGEMM_ERR_UNSUPPORTED); S and Y need 2-byte alignment.
  *  - M == 0 or N == 0 is a no-op returning MPGEMM_OK. K == 0 writes zeros.
- *  - The library reads only the first K elements of each input row and writes
- *    only the first N elements of each output row.
+ *  - Only the first K elements of each input row enter the result, and only
+ *    the first N elements of each output row are written. The fast kernel
+ *    may read (and discard) the bytes of a row up to its next 16-byte
+ *    boundary; such a read never crosses into another page.
  *  - Argument errors return before any HIP call and leave outputs untouched.
  *  - Output rows may not overlap inputs.
  *  - A handle is immutable after creation; calls on different streams may run
@@ -117,8 +123,7 @@ mpgemm_status_t mpgemm_run_i4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K
  * G must be a power of two with 32 <= G <= K and K % G == 0. The sum is
  * accumulated in fp32; where the scale is applied (to the fp16 weight before
  * the product, or to the fp32 group sum after it) is unspecified.
- * S is read as 2-byte elements and needs only 2-byte alignment (the other
- * pointers need 16). */
+ * X and Wq are read with 16-byte loads (see the alignment rule above). */
 mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
                                  const uint16_t *X, int64_t ldx,
                                  const uint8_t *Wq, int64_t ldw,

@@ -45,10 +45,10 @@ mpgemm_status_t check_gemm(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K, c
         return MPGEMM_ERR_UNSUPPORTED;
     if ((lda * elem_num) % elem_den != 0 || (ldb * elem_num) % elem_den != 0)
         return MPGEMM_ERR_UNSUPPORTED;
-    const int64_t lda_b = lda * elem_num / elem_den, ldb_b = ldb * elem_num / elem_den;
-    if ((K > 0 && (!aligned16(A) || !aligned16(B))) || !aligned16(C))
-        return MPGEMM_ERR_UNSUPPORTED;
-    if (lda_b % 16 != 0 || ldb_b % 16 != 0 || (ldc * out_bytes) % 16 != 0)
+    // C is written one element at a time: element alignment suffices. A and B
+    // may have any alignment (rows that are not 16-byte aligned take a slower
+    // byte-gather kernel).
+    if ((reinterpret_cast<uintptr_t>(C) % out_bytes) != 0)
         return MPGEMM_ERR_UNSUPPORTED;
     // the handle is checked last so that every argument error above is
     // reported without a device (and can be tested on a host without a GPU)
@@ -200,9 +200,9 @@ mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_
     if ((ldw % 2) != 0)
         return MPGEMM_ERR_UNSUPPORTED;
     if ((K > 0 && (!aligned16(X) || !aligned16(Wq) || (reinterpret_cast<uintptr_t>(S) & 1u))) ||
-        !aligned16(Y))
+        (reinterpret_cast<uintptr_t>(Y) & 1u))
         return MPGEMM_ERR_UNSUPPORTED;
-    if ((ldx * 2) % 16 != 0 || (ldw / 2) % 16 != 0 || (ldy * 2) % 16 != 0)
+    if ((ldx * 2) % 16 != 0 || (ldw / 2) % 16 != 0)
         return MPGEMM_ERR_UNSUPPORTED;
     if (!h)
         return MPGEMM_ERR_INVALID_ARG;

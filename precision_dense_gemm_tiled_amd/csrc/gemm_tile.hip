@@ -5,9 +5,10 @@
 // into per-wavefront sub-tiles, the same tiling for every precision; a
 // double-buffered pipeline that fetches the next K tile while the current one
 // is multiplied; fragment loads from shared memory feeding the matrix unit.
-// On gfx950 that becomes: coalesced 16-byte global loads of the next K tile
-// into registers, an XOR-swizzled two-stage LDS ring, ds_read_b128 fragments,
-// and v_mfma 32x32 instructions (f16 -> f32, i8 -> i32).
+// On gfx950 that becomes: coalesced 16-byte global loads of future K tiles
+// into registers two tiles ahead, an XOR-swizzled two-stage LDS
+// ring, ds_read_b128 fragments, and v_mfma 32x32 instructions (f16 -> f32,
+// i8 -> i32).
 //
 // INT4 has no matrix instruction on gfx950, so packed nibbles are widened in
 // registers right before the i8 MFMA (the summary's INT4 paragraph: the
@@ -67,44 +68,157 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblk, int tiles_m, in
     tn = in_group / gsize;
 }
 
-// Load one 16-byte chunk of a row, zero-filling bytes at or beyond `limit`
-// (the row's K extent in bytes). `off` is the chunk's byte offset in the row.
-__device__ __forceinline__ i32x4 load_chunk(const uint8_t *row, int64_t off, int64_t limit,
-                                            bool row_ok) {
-    i32x4 v = {0, 0, 0, 0};
-    if (row_ok && off < limit) {
-        if (off + 16 <= limit) {
-            v = *reinterpret_cast<const i32x4 *>(row + off);
-        } else {
-            // ragged K tail: only whole elements exist past this point, byte
-            // granularity covers every precision
-            uint8_t b[16];
+// Zero the bytes of a 16-byte chunk at positions >= nvalid (0 <= nvalid <= 16).
+__device__ __forceinline__ i32x4 keep_bytes(i32x4 v, int nvalid) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                b[i] = (off + i < limit) ? row[off + i] : 0;
-            v = *reinterpret_cast<const i32x4 *>(b);
-        }
+    for (int d = 0; d < 4; ++d) {
+        int nb = nvalid - 4 * d;
+        uint32_t m = nb >= 4 ? 0xFFFFFFFFu : (nb <= 0 ? 0u : ((1u << (8 * nb)) - 1u));
+        v[d] &= (int)m;
     }
     return v;
 }
 
+// Chunk load with K masking for 16-byte aligned rows. A chunk whose first
+// byte lies in the row is read whole: it is 16-byte aligned, so it cannot
+// cross a page boundary, and the bytes past the row's K extent are cleared in
+// registers.
+__device__ __forceinline__ i32x4 load_chunk_masked(const uint8_t *row, int64_t off, int64_t limit,
+                                                   bool row_ok) {
+    i32x4 v = {0, 0, 0, 0};
+    if (row_ok && off < limit) {
+        v = *reinterpret_cast<const i32x4 *>(row + off);
+        if (off + 16 > limit)
+            v = keep_bytes(v, (int)(limit - off));
+    }
+    return v;
+}
+
+// Chunk load for rows with no alignment guarantee: byte gathers.
+__device__ __forceinline__ i32x4 load_chunk_bytes(const uint8_t *row, int64_t off, int64_t limit,
+                                                  bool row_ok) {
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (row_ok) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (off + i < limit)
+                w[i >> 2] |= (uint32_t)row[off + i] << (8 * (i & 3));
+    }
+    return i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+}
+
+// MFMAs of one k-step (32 bytes of K per row: one chunk per lane group) on
+// fragments already in registers.
+template <int P, int TM, int TN>
+__device__ __forceinline__ void mfma_step(const i32x4 (&a)[TM], const i32x4 (&b)[TN],
+                                          typename AccOf<P>::type (&acc)[TM][TN]) {
+    if constexpr (P == PREC_I8) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+    } else if constexpr (P == PREC_F16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    __builtin_bit_cast(f16x8, a[i]), __builtin_bit_cast(f16x8, b[j]), acc[i][j],
+                    0, 0, 0);
+    } else {
+        const int M4 = (int)0xF0F0F0F0u;
+        i32x4 bh[TN], bl[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            bh[j] = b[j] & M4;
+            bl[j] = (b[j] << 4) & M4;
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const i32x4 ah = a[i] & M4;
+            const i32x4 al = (a[i] << 4) & M4;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ah, bh[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(al, bl[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// ds_read_b128 fragments of one k-step (32 bytes of K per row, one 16-byte
+// chunk per lane group) of an LDS stage.
+template <int BM, int BKB, int TM, int TN>
+__device__ __forceinline__ void read_frags(const uint8_t *As, int step, int wm0, int wn0, int lane,
+                                           i32x4 (&a)[TM], i32x4 (&b)[TN]) {
+    constexpr int CPR = BKB / 16;
+    const uint8_t *Bs = As + BM * BKB;
+    const int c = 2 * step + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        int r = wm0 + i * 32 + (lane & 31);
+        a[i] = *reinterpret_cast<const i32x4 *>(As + r * BKB + ((c ^ swz<CPR>(r)) * 16));
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        int r = wn0 + j * 32 + (lane & 31);
+        b[j] = *reinterpret_cast<const i32x4 *>(Bs + r * BKB + ((c ^ swz<CPR>(r)) * 16));
+    }
+}
+
+// Epilogue. 32x32 accumulator layout: register r of lane l holds
+// row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the 32x32 block.
+template <int P, int TM, int TN>
+__device__ __forceinline__ void store_tile(const GemmProblem &p, int row0, int col0, int lane,
+                                           const typename AccOf<P>::type (&acc)[TM][TN]) {
+    typedef typename AccOf<P>::out out_t;
+    out_t *C = reinterpret_cast<out_t *>(p.C);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = col0 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (row < p.M && col < p.N) {
+                    if constexpr (P == PREC_I4)
+                        C[(int64_t)row * p.ldc + col] = acc[i][j][r] >> 8;
+                    else
+                        C[(int64_t)row * p.ldc + col] = acc[i][j][r];
+                }
+            }
+        }
+}
+
+// Main kernel for 16-byte aligned operands whose BM (BN) rows span less than
+// 2^31 bytes. Each thread stages the same 16-byte chunk column c of rows
+// r0 + i * RS of the A and B tiles, so its addresses are one uniform block
+// base plus one 32-bit offset per chunk, and its LDS slots one base plus
+// immediates (the XOR swizzle is the same for rows RS apart).
 template <int P, int BM, int BN, int BKB, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p, int tiles_m,
                                                                    int tiles_n) {
+    constexpr int PF = 2;
     constexpr int NT = 64 * WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     constexpr int CPR = BKB / 16;
-    constexpr int A_PER_T = BM * CPR / NT, B_PER_T = BN * CPR / NT;
+    constexpr int RS = NT / CPR;
+    constexpr int A_PER_T = BM / RS, B_PER_T = BN / RS;
+    constexpr int NL = A_PER_T + B_PER_T;
     constexpr int STAGE = (BM + BN) * BKB;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
-    static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "staging must divide evenly");
+    static_assert(NT % CPR == 0 && BM % RS == 0 && BN % RS == 0, "staging must divide evenly");
+    static_assert(RS % 16 == 0, "swizzle must repeat every RS rows");
     static_assert(CPR % 2 == 0, "two lane groups read adjacent chunks");
+    constexpr int STEPS = CPR / 2;
+    static_assert(STEPS % 2 == 0, "k-steps per stage alternate two fragment buffers");
     // LDS budget, checked at build time (160 KiB per workgroup on gfx950).
     static_assert(2 * STAGE <= 160 * 1024, "LDS ring exceeds 160 KiB");
 
     typedef typename AccOf<P>::type acc_t;
-    typedef typename AccOf<P>::out out_t;
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
@@ -119,43 +233,81 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p
     const int row0 = tm * BM, col0 = tn * BN;
 
     const int64_t kbytes = p.kbytes;
-    const int KT = (int)((kbytes + BKB - 1) / BKB);
+    const int KF = (int)(kbytes / BKB);     // full K tiles
+    const bool tail = (kbytes % BKB) != 0;  // plus one partial tile
+    // Tile sequence: NPRE leading special entries (an all-zero pad that makes
+    // the count a multiple of PF, then the partial tile), then the full tiles
+    // in order. The special entries are all fetched in the prologue, so the
+    // loop body holds only unmasked loads and a single MFMA call site per
+    // stage (which keeps the 256 accumulator registers in place).
+    const int KT = (KF + (tail ? 1 : 0) + PF - 1) / PF * PF;
+    const int NPRE = KT - KF;
 
-    // Per-thread staging: chunk q = i * NT + tid of the A (then B) tile.
-    i32x4 stg[A_PER_T + B_PER_T];
+    const int c = tid % CPR, r0 = tid / CPR;
+    const uint8_t *Ab = p.A + (int64_t)row0 * p.lda_b;
+    const uint8_t *Bb = p.B + (int64_t)col0 * p.ldb_b;
+    const int a_rows = p.M - row0, b_rows = p.N - col0;   // >= 1
+    uint32_t off[NL];
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+        int r = r0 + i * RS;
+        r = r < a_rows ? r : a_rows - 1;   // clamped rows feed outputs never stored
+        off[i] = (uint32_t)r * (uint32_t)p.lda_b + c * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) {
+        int r = r0 + i * RS;
+        r = r < b_rows ? r : b_rows - 1;
+        off[A_PER_T + i] = (uint32_t)r * (uint32_t)p.ldb_b + c * 16;
+    }
+    const int lds0 = r0 * BKB + ((c ^ swz<CPR>(r0)) * 16);
+    // In-loop prefetches are issued unconditionally (a conditional load makes
+    // the compiler's wait counts conservative); past the last full tile they
+    // re-read it, and with no full tile at all they read the first chunk of
+    // the row, which is in bounds. The duplicate data is never consumed.
+    const int klast = KF > 0 ? KF - 1 : 0;
+    const uint32_t cdrop = KF > 0 ? 0u : (uint32_t)(c * 16);
 
-    auto load_tile = [&](int kt) {
+    auto load_fast = [&](int kt, i32x4 *R) {
+        const uint8_t *a = Ab + (int64_t)kt * BKB;
+        const uint8_t *b = Bb + (int64_t)kt * BKB;
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i)
+            R[i] = *reinterpret_cast<const i32x4 *>(a + off[i]);
+#pragma unroll
+        for (int i = 0; i < B_PER_T; ++i)
+            R[A_PER_T + i] = *reinterpret_cast<const i32x4 *>(b + off[A_PER_T + i]);
+    };
+    auto load_fast_clamped = [&](int kt, i32x4 *R) {
+        const int k = kt < klast ? kt : klast;
+        const uint8_t *a = Ab + (int64_t)k * BKB;
+        const uint8_t *b = Bb + (int64_t)k * BKB;
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i)
+            R[i] = *reinterpret_cast<const i32x4 *>(a + (off[i] - cdrop));
+#pragma unroll
+        for (int i = 0; i < B_PER_T; ++i)
+            R[A_PER_T + i] = *reinterpret_cast<const i32x4 *>(b + (off[A_PER_T + i] - cdrop));
+    };
+    auto load_tail = [&](int kt, i32x4 *R) {
         const int64_t k0 = (int64_t)kt * BKB;
 #pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) {
-            int q = i * NT + tid, r = q / CPR, c = q % CPR;
-            int gr = row0 + r;
-            bool ok = gr < p.M;
-            const uint8_t *rowp = p.A + (int64_t)(ok ? gr : 0) * p.lda_b;
-            stg[i] = load_chunk(rowp, k0 + c * 16, kbytes, ok);
-        }
+        for (int i = 0; i < A_PER_T; ++i)
+            R[i] = load_chunk_masked(Ab + off[i] - c * 16, k0 + c * 16, kbytes,
+                                     r0 + i * RS < a_rows);
 #pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) {
-            int q = i * NT + tid, r = q / CPR, c = q % CPR;
-            int gr = col0 + r;
-            bool ok = gr < p.N;
-            const uint8_t *rowp = p.B + (int64_t)(ok ? gr : 0) * p.ldb_b;
-            stg[A_PER_T + i] = load_chunk(rowp, k0 + c * 16, kbytes, ok);
-        }
+        for (int i = 0; i < B_PER_T; ++i)
+            R[A_PER_T + i] = load_chunk_masked(Bb + off[A_PER_T + i] - c * 16, k0 + c * 16, kbytes,
+                                               r0 + i * RS < b_rows);
     };
-    auto store_tile = [&](int stage) {
-        uint8_t *As = smem + stage * STAGE;
-        uint8_t *Bs = As + BM * BKB;
+    auto store = [&](int stage, const i32x4 *R) {
+        uint8_t *S = smem + stage * STAGE + lds0;
 #pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) {
-            int q = i * NT + tid, r = q / CPR, c = q % CPR;
-            *reinterpret_cast<i32x4 *>(As + r * BKB + ((c ^ swz<CPR>(r)) * 16)) = stg[i];
-        }
+        for (int i = 0; i < A_PER_T; ++i)
+            *reinterpret_cast<i32x4 *>(S + i * RS * BKB) = R[i];
 #pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) {
-            int q = i * NT + tid, r = q / CPR, c = q % CPR;
-            *reinterpret_cast<i32x4 *>(Bs + r * BKB + ((c ^ swz<CPR>(r)) * 16)) = stg[A_PER_T + i];
-        }
+        for (int i = 0; i < B_PER_T; ++i)
+            *reinterpret_cast<i32x4 *>(S + BM * BKB + i * RS * BKB) = R[A_PER_T + i];
     };
 
     acc_t acc[TM][TN];
@@ -165,106 +317,159 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p
         for (int j = 0; j < TN; ++j)
             acc[i][j] = acc_t{};
 
-    auto compute = [&](int stage) {
-        const uint8_t *As = smem + stage * STAGE;
-        const uint8_t *Bs = As + BM * BKB;
-        const int g = lane >> 5;
+    // prologue only: any entry of the sequence
+    auto load_entry = [&](int e, i32x4 *R) {
+        if (e >= NPRE) {
+            load_fast(e - NPRE, R);
+        } else if (tail && e == NPRE - 1) {
+            load_tail(KF, R);
+        } else {
 #pragma unroll
-        for (int kc = 0; kc < CPR; kc += 2) {
-            const int c = kc + g;
-            i32x4 a[TM], b[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                int r = wm0 + i * 32 + (lane & 31);
-                a[i] = *reinterpret_cast<const i32x4 *>(As + r * BKB + ((c ^ swz<CPR>(r)) * 16));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                int r = wn0 + j * 32 + (lane & 31);
-                b[j] = *reinterpret_cast<const i32x4 *>(Bs + r * BKB + ((c ^ swz<CPR>(r)) * 16));
-            }
-            if constexpr (P == PREC_I8) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-            } else if constexpr (P == PREC_F16) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(f16x8, a[i]), __builtin_bit_cast(f16x8, b[j]),
-                            acc[i][j], 0, 0, 0);
-            } else {
-                const int M4 = (int)0xF0F0F0F0u;
-                i32x4 ah[TM], al[TM], bh[TN], bl[TN];
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    ah[i] = a[i] & M4;
-                    al[i] = (a[i] << 4) & M4;
-                }
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    bh[j] = b[j] & M4;
-                    bl[j] = (b[j] << 4) & M4;
-                }
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ah[i], bh[j], acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(al[i], bl[j], acc[i][j], 0, 0, 0);
-                    }
-            }
+            for (int i = 0; i < NL; ++i)
+                R[i] = i32x4{0, 0, 0, 0};
         }
     };
 
+    // Software pipeline. Entry t of the tile sequence is fetched from global
+    // memory into register set t % 2 two entries ahead of its use, written to
+    // LDS stage t % 2 one entry ahead, and read as fragments one k-step ahead
+    // of its MFMAs. The LDS write and the barrier that publishes the next stage
+    // sit before the last k-step's MFMAs, which then hide the barrier and the
+    // first fragment reads of the next stage. sched_barrier(0) pins this order
+    // against the compiler's scheduler.
+    i32x4 R0[NL], R1[NL];
+    i32x4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     if (KT > 0) {
-        load_tile(0);
-        store_tile(0);
+        load_entry(0, R0);
+        store(0, R0);
+        load_entry(1, R1);
+    }
+    __syncthreads();
+    read_frags<BM, BKB, TM, TN>(smem, 0, wm0, wn0, lane, fa0, fb0);
+
+    // one pipeline entry held in LDS stage `stage`; Rload receives entry
+    // kt_next from global memory, Rstore (entry + 1) goes to the other stage
+    auto entry = [&](int stage, i32x4 (&Rload)[NL], int kt_next, const i32x4 (&Rstore)[NL]) {
+        const uint8_t *S = smem + stage * STAGE;
+        load_fast_clamped(kt_next, Rload);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int step = 0; step < STEPS; step += 2) {
+            // even step: fragments in buffer 0; prefetch step + 1 into buffer 1
+            read_frags<BM, BKB, TM, TN>(S, step + 1, wm0, wn0, lane, fa1, fb1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step<P, TM, TN>(fa0, fb0, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            // odd step: fragments in buffer 1; prefetch into buffer 0 either
+            // step + 2 or, at the last step, step 0 of the next stage
+            if (step + 2 < STEPS) {
+                read_frags<BM, BKB, TM, TN>(S, step + 2, wm0, wn0, lane, fa0, fb0);
+            } else {
+                store(stage ^ 1, Rstore);
+                __syncthreads();
+                read_frags<BM, BKB, TM, TN>(smem + (stage ^ 1) * STAGE, 0, wm0, wn0, lane, fa0, fb0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step<P, TM, TN>(fa1, fb1, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    for (int kt = 0; kt < KT; kt += 2) {
+        entry(0, R0, kt + 2 - NPRE, R1);   // entry kt; R1 holds entry kt + 1
+        entry(1, R1, kt + 3 - NPRE, R0);   // entry kt + 1; R0 holds entry kt + 2
+    }
+    store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc);
+}
+
+// Operands without 16-byte row alignment (or with rows too long for 32-bit
+// offsets): byte-gather loads, 64-bit addressing, single prefetch.
+template <int P, int BM, int BN, int BKB, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_generic_kernel(GemmProblem p,
+                                                                           int tiles_m,
+                                                                           int tiles_n) {
+    constexpr int NT = 64 * WGM * WGN;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int CPR = BKB / 16;
+    constexpr int RS = NT / CPR;
+    constexpr int A_PER_T = BM / RS, B_PER_T = BN / RS;
+    constexpr int NL = A_PER_T + B_PER_T;
+    constexpr int STAGE = (BM + BN) * BKB;
+    static_assert(RS % 16 == 0 && BM % RS == 0 && BN % RS == 0, "staging must divide evenly");
+    typedef typename AccOf<P>::type acc_t;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / WGN) * WTM, wn0 = (wave % WGN) * WTN;
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int row0 = tm * BM, col0 = tn * BN;
+    const int64_t kbytes = p.kbytes;
+    const int KT = (int)((kbytes + BKB - 1) / BKB);
+    const int c = tid % CPR, r0 = tid / CPR;
+    const int lds0 = r0 * BKB + ((c ^ swz<CPR>(r0)) * 16);
+
+    auto load = [&](int kt, i32x4 *R) {
+        const int64_t k = (int64_t)kt * BKB + c * 16;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const bool isA = i < A_PER_T;
+            const int gr = (isA ? row0 : col0) + r0 + (isA ? i : i - A_PER_T) * RS;
+            const bool ok = gr < (isA ? p.M : p.N);
+            const uint8_t *row = (isA ? p.A : p.B) + (int64_t)(ok ? gr : 0) * (isA ? p.lda_b : p.ldb_b);
+            R[i] = load_chunk_bytes(row, k, kbytes, ok);
+        }
+    };
+    auto store = [&](int stage, const i32x4 *R) {
+        uint8_t *S = smem + stage * STAGE + lds0;
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i)
+            *reinterpret_cast<i32x4 *>(S + i * RS * BKB) = R[i];
+#pragma unroll
+        for (int i = 0; i < B_PER_T; ++i)
+            *reinterpret_cast<i32x4 *>(S + BM * BKB + i * RS * BKB) = R[A_PER_T + i];
+    };
+
+    acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = acc_t{};
+    i32x4 R[NL];
+    if (KT > 0) {
+        load(0, R);
+        store(0, R);
     }
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
         if (kt + 1 < KT)
-            load_tile(kt + 1);
-        compute(cur);
+            load(kt + 1, R);
+#pragma unroll
+        for (int step = 0; step < CPR / 2; ++step) {
+            i32x4 fa[TM], fb[TN];
+            read_frags<BM, BKB, TM, TN>(smem + cur * STAGE, step, wm0, wn0, lane, fa, fb);
+            mfma_step<P, TM, TN>(fa, fb, acc);
+        }
         if (kt + 1 < KT)
-            store_tile(cur ^ 1);
+            store(cur ^ 1, R);
         __syncthreads();
     }
-
-    // Epilogue. 32x32 accumulator layout: register r of lane l holds
-    // row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the 32x32 block.
-    out_t *C = reinterpret_cast<out_t *>(p.C);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = col0 + wn0 + j * 32 + (lane & 31);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = row0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (row < p.M && col < p.N) {
-                    if constexpr (P == PREC_I4)
-                        C[(int64_t)row * p.ldc + col] = acc[i][j][r] >> 8;
-                    else
-                        C[(int64_t)row * p.ldc + col] = acc[i][j][r];
-                }
-            }
-        }
+    store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc);
 }
 
 // ------------------------------------------------------------------ launch
 
 struct CfgShape { int BM, BN; const char *name; };
 static const CfgShape kCfg[CFG_COUNT] = {
-    {256, 256, "256x256x64B_w2x2"},
-    {128, 128, "128x128x64B_w2x2"},
-    {64, 64, "64x64x128B_w2x2"},
-    {256, 128, "256x128x64B_w2x2"},
+    {256, 256, "256x256_bk64"},
+    {128, 128, "128x128_bk64"},
+    {64, 64, "64x64_bk128"},
+    {256, 128, "256x128_bk64"},
+    {256, 256, "256x256_bk128"},
+    {128, 256, "128x256_bk64"},
+    {128, 128, "128x128_bk128"},
 };
 
 const char *tile_cfg_name(int cfg) {
@@ -297,21 +502,37 @@ static hipError_t launch_one(const GemmProblem &p, hipStream_t stream) {
 }
 
 template <int P>
-static hipError_t launch_prec(int cfg, const GemmProblem &p, hipStream_t stream) {
+static hipError_t launch_prec(int cfg, const GemmProblem &p, bool aligned, hipStream_t stream) {
+    if (!aligned) {   // byte-gather loads, one shape
+        constexpr int BM = 128, BN = 128;
+        int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+        hipLaunchKernelGGL((gemm_tile_generic_kernel<P, BM, BN, 64, 2, 2>), dim3(tiles_m * tiles_n),
+                           dim3(256), 0, stream, p, tiles_m, tiles_n);
+        return hipGetLastError();
+    }
     switch (cfg) {
     case CFG_256x256: return launch_one<P, 256, 256, 64, 2, 2>(p, stream);
     case CFG_128x128: return launch_one<P, 128, 128, 64, 2, 2>(p, stream);
     case CFG_64x64: return launch_one<P, 64, 64, 128, 2, 2>(p, stream);
     case CFG_256x128: return launch_one<P, 256, 128, 64, 2, 2>(p, stream);
+    case CFG_256x256_BK128: return launch_one<P, 256, 256, 128, 2, 2>(p, stream);
+    case CFG_128x256: return launch_one<P, 128, 256, 64, 2, 2>(p, stream);
+    case CFG_128x128_BK128: return launch_one<P, 128, 128, 128, 2, 2>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_gemm(int prec, int cfg, const GemmProblem &p, hipStream_t stream) {
+    // The fast kernel needs 16-byte aligned rows and 32-bit offsets within the
+    // 256 rows of a tile.
+    const int64_t kRowLimit = (int64_t)1 << 23;
+    const bool aligned = (reinterpret_cast<uintptr_t>(p.A) % 16 == 0) &&
+                         (reinterpret_cast<uintptr_t>(p.B) % 16 == 0) && p.lda_b % 16 == 0 &&
+                         p.ldb_b % 16 == 0 && p.lda_b < kRowLimit && p.ldb_b < kRowLimit;
     switch (prec) {
-    case PREC_F16: return launch_prec<PREC_F16>(cfg, p, stream);
-    case PREC_I8: return launch_prec<PREC_I8>(cfg, p, stream);
-    case PREC_I4: return launch_prec<PREC_I4>(cfg, p, stream);
+    case PREC_F16: return launch_prec<PREC_F16>(cfg, p, aligned, stream);
+    case PREC_I8: return launch_prec<PREC_I8>(cfg, p, aligned, stream);
+    case PREC_I4: return launch_prec<PREC_I4>(cfg, p, aligned, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -78,11 +78,13 @@ A, B, C, S = 0x10000, 0x20000, 0x30000, 0x40000
     # leading dimensions
     (("i8", 4, 4, 32, A, 16, B, 32, C, 16), 1),
     (("f16", 4, 8, 16, A, 16, B, 16, C, 4), 1),
-    # alignment of pointers and row strides
-    (("i8", 4, 4, 16, A + 4, 16, B, 16, C, 16), 2),
-    (("i8", 4, 4, 16, A, 24, B, 16, C, 16), 2),
-    (("f16", 4, 4, 16, A, 20, B, 16, C, 16), 2),
-    (("f16", 4, 6, 16, A, 16, B, 16, C, 6), 2),
+    # unaligned operands are accepted (byte-gather kernel); C needs 4 bytes
+    (("i8", 4, 4, 16, A + 4, 16, B, 16, C, 16), 1),
+    (("i8", 4, 4, 16, A, 24, B, 16, C, 16), 1),
+    (("f16", 4, 4, 16, A, 20, B, 16, C, 16), 1),
+    (("f16", 4, 6, 16, A, 16, B, 16, C, 6), 1),
+    (("f16", 4, 4, 16, A, 16, B, 16, C + 2, 16), 2),
+    (("i8", 4, 4, 16, A, 16, B, 16, C + 1, 16), 2),
     # INT4: odd K or odd ld
     (("i4", 4, 4, 31, A, 32, B, 32, C, 16), 2),
     (("i4", 4, 4, 32, A, 33, B, 32, C, 16), 2),
@@ -107,6 +109,9 @@ def test_gemm_argument_errors_without_device(mp, call, expect):
     ((1, 16, 256, A, 256, B, 256, S + 1, 2, 128, C, 16), 2),  # scales not 2-byte aligned
     ((1, 16, 256, A, 256, B, 250, S, 2, 128, C, 16), 1),     # ldw < K
     ((1, 16, 256, A, 260, B, 256, S, 2, 128, C, 16), 2),     # X row stride not 16 B
+    ((1, 16, 256, A + 2, 256, B, 256, S, 2, 128, C, 16), 2),  # X not 16-byte aligned
+    ((1, 16, 256, A, 256, B, 256, S, 2, 128, C + 1, 16), 2),  # Y not 2-byte aligned
+    ((1, 10, 256, A, 256, B, 256, S, 2, 128, C + 2, 10), 1),  # any Y stride: NULL handle left
     ((0, 16, 256, 0, 256, 0, 256, 0, 2, 128, 0, 16), 0),     # M = 0: no-op
 ])
 def test_w4a16_argument_errors_without_device(mp, args, expect):
