@@ -52,87 +52,111 @@ __device__ __forceinline__ f16x8 perm8(f16x8 x) {
     return __builtin_shufflevector(x, x, 0, 4, 1, 5, 2, 6, 3, 7);
 }
 
+// Loads and MFMAs of UU consecutive 128-k steps starting at step s0 for one
+// wavefront (16 weight rows, MT blocks of 16 activation rows). Every load is
+// issued before any is consumed, from clamped (always valid) addresses, so
+// the loads stay in flight together; rows past M or N only feed results that
+// are never stored. With KFULL false, lane groups whose 32-k run lies past K
+// zero their weights and activations at use time.
+template <int MT, int UU, bool SCALE_AFTER, bool KFULL>
+__device__ __forceinline__ void w4a16_steps(const W4A16Problem &p, int s0, int lane, int nrow_c,
+                                            int m0, int lg, f32x4 (&acc)[MT]) {
+    const int g = lane >> 4;
+    const uint8_t *wrow = p.W + (int64_t)nrow_c * p.ldw_b;
+    const uint16_t *srow = p.S + (int64_t)nrow_c * p.lds;
+    i32x4 wv[UU];
+    _Float16 sc[UU];
+    f16x8 xv[UU][MT][4];
+    bool k_ok[UU];
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        int kl = (s0 + u) * 128 + g * 32;
+        k_ok[u] = KFULL || kl < p.K;
+        kl = (KFULL || kl < p.K) ? kl : p.K - 32;
+        wv[u] = *reinterpret_cast<const i32x4 *>(wrow + kl / 2);
+        sc[u] = __builtin_bit_cast(_Float16, srow[kl >> lg]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            int mrow = m0 + mt * 16 + (lane & 15);
+            mrow = mrow < p.M ? mrow : p.M - 1;
+            const f16x8 *xp = reinterpret_cast<const f16x8 *>(p.X + (int64_t)mrow * p.ldx + kl);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                xv[u][mt][t] = xp[t];
+        }
+    }
+    // keep the scheduler from interleaving the load phase with the math
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        if constexpr (!KFULL) {
+            if (!k_ok[u]) {
+                wv[u] = i32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        xv[u][mt][t] = f16x8{};
+            }
+        }
+        f16x8 wq[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            wq[t] = dequant8((uint32_t)wv[u][t]);
+            if constexpr (!SCALE_AFTER) {
+                const f16x8 s8 = {sc[u], sc[u], sc[u], sc[u], sc[u], sc[u], sc[u], sc[u]};
+                wq[t] = wq[t] * s8;
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (SCALE_AFTER) {
+                f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    part = __builtin_amdgcn_mfma_f32_16x16x32_f16(perm8(xv[u][mt][t]), wq[t], part, 0, 0, 0);
+                const float sf = (float)sc[u];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[mt][r] += part[r] * sf;
+            } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(perm8(xv[u][mt][t]), wq[t], acc[mt], 0, 0, 0);
+            }
+        }
+    }
+}
+
 // MT: 16-row activation blocks per wavefront; WN: wavefronts along N (16 weight
 // rows each); WK: wavefronts splitting K (reduced through LDS at the end);
 // U: steps whose loads are issued before any of them is consumed.
-template <int MT, int WN, int WK, int U, bool SCALE_AFTER>
-__global__ __launch_bounds__(64 * WN * WK) void w4a16_kernel(W4A16Problem p) {
+template <int MT, int WN, int WK, int U, bool SCALE_AFTER, bool KFULL>
+__global__ __launch_bounds__(64 * WN * WK) void w4a16_kernel(W4A16Problem p, int lg) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wn = wave % WN, wk = wave / WN;
     const int n0 = blockIdx.x * (16 * WN) + wn * 16;
     const int m0 = blockIdx.y * (16 * MT);
     const int nrow = n0 + (lane & 15);
+    const int nrow_c = nrow < p.N ? nrow : p.N - 1;
     const int g = lane >> 4;
-    const bool n_ok = nrow < p.N;
 
     const int steps = (p.K + 127) / 128;
     const int per_wave = (steps + WK - 1) / WK;
     const int s_begin = wk * per_wave;
     const int s_end = min(steps, s_begin + per_wave);
 
-    const uint8_t *wrow = p.W + (int64_t)(n_ok ? nrow : 0) * p.ldw_b;
-    const uint16_t *srow = p.S + (int64_t)(n_ok ? nrow : 0) * p.lds;
-
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int s0 = s_begin; s0 < s_end; s0 += U) {
-        i32x4 wv[U];
-        _Float16 sc[U];
-        f16x8 xv[U][MT][4];
-        // issue every load of the U steps first
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int s = s0 + u;
-            const int kl = s * 128 + g * 32;
-            const bool k_ok = (s < s_end) && (kl < p.K);
-            wv[u] = (n_ok && k_ok) ? *reinterpret_cast<const i32x4 *>(wrow + kl / 2)
-                                   : i32x4{0, 0, 0, 0};
-            sc[u] = (n_ok && k_ok) ? __builtin_bit_cast(_Float16, srow[kl / p.G]) : (_Float16)0.0f;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int mrow = m0 + mt * 16 + (lane & 15);
-                const bool ok = k_ok && mrow < p.M;
-                const f16x8 *xp = reinterpret_cast<const f16x8 *>(
-                    p.X + (int64_t)(ok ? mrow : 0) * p.ldx + (ok ? kl : 0));
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    xv[u][mt][t] = ok ? xp[t] : f16x8{};
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            f16x8 wq[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                wq[t] = dequant8((uint32_t)wv[u][t]);
-                if constexpr (!SCALE_AFTER) {
-                    const f16x8 s8 = {sc[u], sc[u], sc[u], sc[u], sc[u], sc[u], sc[u], sc[u]};
-                    wq[t] = wq[t] * s8;
-                }
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                if constexpr (SCALE_AFTER) {
-                    f32x4 part = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        part = __builtin_amdgcn_mfma_f32_16x16x32_f16(perm8(xv[u][mt][t]), wq[t], part, 0, 0, 0);
-                    const float sf = (float)sc[u];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[mt][r] += part[r] * sf;
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(perm8(xv[u][mt][t]), wq[t], acc[mt], 0, 0, 0);
-                }
-            }
-        }
-    }
+    int s0 = s_begin;
+    for (; s0 + U <= s_end; s0 += U)
+        w4a16_steps<MT, U, SCALE_AFTER, KFULL>(p, s0, lane, nrow_c, m0, lg, acc);
+    for (; s0 < s_end; ++s0)
+        w4a16_steps<MT, 1, SCALE_AFTER, KFULL>(p, s0, lane, nrow_c, m0, lg, acc);
 
     // Reduce the WK partial sums (16x16 accumulator layout: register r of
     // lane l holds row 4*(l/16) + r, column l%16).
@@ -149,7 +173,7 @@ __global__ __launch_bounds__(64 * WN * WK) void w4a16_kernel(W4A16Problem p) {
             for (int o = 1; o < WK; ++o)
                 acc[mt] += red[o][wn][mt][lane];
     }
-    if (!n_ok)
+    if (nrow >= p.N)
         return;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -165,10 +189,16 @@ template <int MT, int WN, int WK, int U>
 static hipError_t launch_cfg(const W4A16Problem &p, hipStream_t stream) {
     dim3 block(64 * WN * WK);
     dim3 grid((p.N + 16 * WN - 1) / (16 * WN), (p.M + 16 * MT - 1) / (16 * MT));
+    int lg = 0;
+    while ((1 << lg) < p.G)
+        ++lg;
+    // G % 128 == 0 implies K % 128 == 0: every step lies in one group
     if (p.G % 128 == 0)
-        hipLaunchKernelGGL((w4a16_kernel<MT, WN, WK, U, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((w4a16_kernel<MT, WN, WK, U, true, true>), grid, block, 0, stream, p, lg);
+    else if (p.K % 128 == 0)
+        hipLaunchKernelGGL((w4a16_kernel<MT, WN, WK, U, false, true>), grid, block, 0, stream, p, lg);
     else
-        hipLaunchKernelGGL((w4a16_kernel<MT, WN, WK, U, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((w4a16_kernel<MT, WN, WK, U, false, false>), grid, block, 0, stream, p, lg);
     return hipGetLastError();
 }
 
