@@ -240,6 +240,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["f16", "i8", "i4", "w4a16"], default=None,
                     help="time only this precision's sweep (no headline line)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run one plain 256 MiB device copy (reference dispatch for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -253,6 +256,16 @@ def main():
         raise SystemExit("bench.py needs a gfx950 GPU")
     mp.lib()
     torch.cuda.set_device(0)
+
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+        log("[bench] calibration copy of 268435456 bytes done")
 
     if args.only:
         precs = [args.only]
