@@ -240,6 +240,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["f16", "i8", "i4", "w4a16"], default=None,
                     help="time only this precision's sweep (no headline line)")
+    ap.add_argument("--sizes", type=str, default=None,
+                    help="with --only: comma-separated sizes (N, or M for w4a16)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 256 MiB device copy (reference dispatch for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -272,6 +274,8 @@ def main():
         out = {}
         for prec in precs:
             sizes = W4A16_M if prec == "w4a16" else SQUARE_SIZES
+            if args.sizes:
+                sizes = [int(v) for v in args.sizes.split(",")]
             out[prec] = []
             for s in sizes:
                 M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else (s, s, s)

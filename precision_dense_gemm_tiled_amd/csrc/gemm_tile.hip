@@ -108,44 +108,32 @@ __device__ __forceinline__ i32x4 load_chunk_bytes(const uint8_t *row, int64_t of
 }
 
 // MFMAs of one k-step (32 bytes of K per row: one chunk per lane group) on
-// fragments already in registers.
-template <int P, int TM, int TN>
+// fragments already in registers, restricted to the blocks (i, j) whose flat
+// index i * TN + j lies in [LO, HI).
+template <int P, int TM, int TN, int LO = 0, int HI = TM * TN>
 __device__ __forceinline__ void mfma_step(const i32x4 (&a)[TM], const i32x4 (&b)[TN],
                                           typename AccOf<P>::type (&acc)[TM][TN]) {
-    if constexpr (P == PREC_I8) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-    } else if constexpr (P == PREC_F16) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    __builtin_bit_cast(f16x8, a[i]), __builtin_bit_cast(f16x8, b[j]), acc[i][j],
-                    0, 0, 0);
-    } else {
-        const int M4 = (int)0xF0F0F0F0u;
-        i32x4 bh[TN], bl[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            bh[j] = b[j] & M4;
-            bl[j] = (b[j] << 4) & M4;
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const i32x4 ah = a[i] & M4;
-            const i32x4 al = (a[i] << 4) & M4;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ah, bh[j], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(al, bl[j], acc[i][j], 0, 0, 0);
-            }
+    for (int f = LO; f < HI; ++f) {
+        const int i = f / TN, j = f % TN;
+        if constexpr (P == PREC_I8) {
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+        } else if constexpr (P == PREC_F16) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, a[i]), __builtin_bit_cast(f16x8, b[j]), acc[i][j], 0, 0, 0);
+        } else {
+            // INT4: widen both operands (16 * nibble per byte) right before use
+            const int M4 = (int)0xF0F0F0F0u;
+            const i32x4 ah = a[i] & M4, al = (a[i] << 4) & M4;
+            const i32x4 bh = b[j] & M4, bl = (b[j] << 4) & M4;
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ah, bh, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(al, bl, acc[i][j], 0, 0, 0);
         }
     }
 }
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200;
 
 // ds_read_b128 fragments of one k-step (32 bytes of K per row, one 16-byte
 // chunk per lane group) of an LDS stage.
@@ -347,32 +335,64 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p
     __syncthreads();
     read_frags<BM, BKB, TM, TN>(smem, 0, wm0, wn0, lane, fa0, fb0);
 
-    // one pipeline entry held in LDS stage `stage`; Rload receives entry
-    // kt_next from global memory, Rstore (entry + 1) goes to the other stage
+    // One pipeline entry held in LDS stage `stage`; Rload receives entry
+    // kt_next from global memory, Rstore (entry + 1) goes to the other stage.
+    // Region A (before the barrier): the global loads, the fragment reads of
+    // steps 1.. and the LDS writes are interleaved one by one with the MFMAs
+    // of steps 0 .. STEPS-2 and the first KA MFMAs of the last step. Region B
+    // (after the barrier): the next stage's step-0 fragment reads interleaved
+    // with the rest of the last step's MFMAs. Each MFMA occupies the matrix
+    // pipe for several cycles, so the memory instructions issue in its shadow.
+    constexpr int NMF = TM * TN;               // MFMAs per k-step per operand pair
+    constexpr int MFI = (P == PREC_I4) ? 2 : 1; // MFMA instructions per (i, j)
+    constexpr int NFR = TM + TN;                // fragment reads per k-step
+    constexpr int KA = NMF >= 4 ? NMF / 4 : 1;  // last-step MFMAs before the barrier
+    constexpr int DSW = (NL + KA - 1) / KA;     // LDS writes per MFMA before the barrier
     auto entry = [&](int stage, i32x4 (&Rload)[NL], int kt_next, const i32x4 (&Rstore)[NL]) {
         const uint8_t *S = smem + stage * STAGE;
-        load_fast_clamped(kt_next, Rload);
         __builtin_amdgcn_sched_barrier(0);
+        load_fast_clamped(kt_next, Rload);
 #pragma unroll
-        for (int step = 0; step < STEPS; step += 2) {
-            // even step: fragments in buffer 0; prefetch step + 1 into buffer 1
-            read_frags<BM, BKB, TM, TN>(S, step + 1, wm0, wn0, lane, fa1, fb1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_step<P, TM, TN>(fa0, fb0, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            // odd step: fragments in buffer 1; prefetch into buffer 0 either
-            // step + 2 or, at the last step, step 0 of the next stage
-            if (step + 2 < STEPS) {
-                read_frags<BM, BKB, TM, TN>(S, step + 2, wm0, wn0, lane, fa0, fb0);
+        for (int step = 0; step < STEPS - 1; ++step) {
+            if (step % 2 == 0) {
+                read_frags<BM, BKB, TM, TN>(S, step + 1, wm0, wn0, lane, fa1, fb1);
+                mfma_step<P, TM, TN>(fa0, fb0, acc);
             } else {
-                store(stage ^ 1, Rstore);
-                __syncthreads();
-                read_frags<BM, BKB, TM, TN>(smem + (stage ^ 1) * STAGE, 0, wm0, wn0, lane, fa0, fb0);
+                read_frags<BM, BKB, TM, TN>(S, step + 1, wm0, wn0, lane, fa0, fb0);
+                mfma_step<P, TM, TN>(fa1, fb1, acc);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_step<P, TM, TN>(fa1, fb1, acc);
-            __builtin_amdgcn_sched_barrier(0);
         }
+        // STEPS is even: the last step's fragments are in buffer 1
+        mfma_step<P, TM, TN, 0, KA>(fa1, fb1, acc);
+        store(stage ^ 1, Rstore);
+        // region A schedule
+#pragma unroll
+        for (int step = 0; step < STEPS - 1; ++step) {
+#pragma unroll
+            for (int f = 0; f < NMF; ++f) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, MFI, 0);
+                if (step == 0 && f < NL)
+                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+                if (f < NFR)
+                    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < KA; ++f) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, MFI, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DS_WR, DSW, 0);
+        }
+        __syncthreads();
+        read_frags<BM, BKB, TM, TN>(smem + (stage ^ 1) * STAGE, 0, wm0, wn0, lane, fa0, fb0);
+        mfma_step<P, TM, TN, KA, NMF>(fa1, fb1, acc);
+        // region B schedule
+#pragma unroll
+        for (int f = KA; f < NMF; ++f) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, MFI, 1);
+            if (f - KA < NFR)
+                __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
     for (int kt = 0; kt < KT; kt += 2) {
         entry(0, R0, kt + 2 - NPRE, R1);   // entry kt; R1 holds entry kt + 1
