@@ -5,10 +5,11 @@
 // into per-wavefront sub-tiles, the same tiling for every precision; a
 // double-buffered pipeline that fetches the next K tile while the current one
 // is multiplied; fragment loads from shared memory feeding the matrix unit.
-// On gfx950 that becomes: coalesced 16-byte global loads of future K tiles
-// into registers two tiles ahead, an XOR-swizzled two-stage LDS
-// ring, ds_read_b128 fragments, and v_mfma 32x32 instructions (f16 -> f32,
-// i8 -> i32).
+// On gfx950 that becomes: coalesced 16-byte direct-to-LDS loads
+// (global_load_lds_dwordx4) of the next K tile into an XOR-swizzled two-stage
+// LDS ring, ds_read_b128 fragments double-buffered in registers, and v_mfma
+// 32x32 instructions (f16 -> f32, i8 -> i32), with the memory instructions
+// issued in the shadow of the MFMAs.
 //
 // INT4 has no matrix instruction on gfx950, so packed nibbles are widened in
 // registers right before the i8 MFMA (the summary's INT4 paragraph: the
@@ -132,9 +133,6 @@ __device__ __forceinline__ void mfma_step(const i32x4 (&a)[TM], const i32x4 (&b)
     }
 }
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200;
-
 // ds_read_b128 fragments of one k-step (32 bytes of K per row, one 16-byte
 // chunk per lane group) of an LDS stage.
 template <int BM, int BKB, int TM, int TN>
@@ -180,35 +178,64 @@ __device__ __forceinline__ void store_tile(const GemmProblem &p, int row0, int c
         }
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).
+// The LDS destination is wave-uniform: lane l writes lds + 16 * l.
+__device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *lds) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// s_waitcnt immediate for "at most VM vector-memory operations outstanding,
+// all LDS operations done" (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 left at its maximum, lgkmcnt 11:8).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lds() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    constexpr int imm = (VM & 15) | ((VM >> 4) << 14) | (7 << 4);
+    __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// Workgroup barrier that publishes LDS-DMA data without waiting for every
+// outstanding load: the caller's wait_vm_lds<> decides which loads must have
+// landed. Compiler-level fences keep memory operations on their side.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Main kernel for 16-byte aligned operands whose BM (BN) rows span less than
-// 2^31 bytes. Each thread stages the same 16-byte chunk column c of rows
-// r0 + i * RS of the A and B tiles, so its addresses are one uniform block
-// base plus one 32-bit offset per chunk, and its LDS slots one base plus
-// immediates (the XOR swizzle is the same for rows RS apart).
-template <int P, int BM, int BN, int BKB, int WGM, int WGN>
+// 2^31 bytes. Full K tiles move from global memory straight into an NS-stage
+// LDS ring with direct-to-LDS loads (no staging registers, no ds_write),
+// NS - 1 tiles ahead of the MFMAs that consume them. One load instruction of
+// a wavefront fills 1 KiB of contiguous LDS, i.e. 64 / CPR whole rows of a
+// tile; lane l lands at row l / CPR, 16-byte slot l % CPR, so it fetches the
+// global chunk that the XOR swizzle puts in that slot. Each thread's rows are
+// r0 + i * RS (RS = NT / CPR), whose swizzle is the same for every i, so its
+// addresses are one uniform block base plus one 32-bit offset per load.
+template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p, int tiles_m,
                                                                    int tiles_n) {
-    constexpr int PF = 2;
     constexpr int NT = 64 * WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     constexpr int CPR = BKB / 16;
     constexpr int RS = NT / CPR;
     constexpr int A_PER_T = BM / RS, B_PER_T = BN / RS;
-    constexpr int NL = A_PER_T + B_PER_T;
+    constexpr int NL = A_PER_T + B_PER_T;   // direct-to-LDS loads per thread per tile
     constexpr int STAGE = (BM + BN) * BKB;
+    constexpr int STEPS = CPR / 2;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(NT % CPR == 0 && BM % RS == 0 && BN % RS == 0, "staging must divide evenly");
     static_assert(RS % 16 == 0, "swizzle must repeat every RS rows");
-    static_assert(CPR % 2 == 0, "two lane groups read adjacent chunks");
-    constexpr int STEPS = CPR / 2;
     static_assert(STEPS % 2 == 0, "k-steps per stage alternate two fragment buffers");
+    static_assert(NS >= 2 && (NS - 2) * NL < 64, "ring depth");
     // LDS budget, checked at build time (160 KiB per workgroup on gfx950).
-    static_assert(2 * STAGE <= 160 * 1024, "LDS ring exceeds 160 KiB");
+    static_assert(NS * STAGE <= 160 * 1024, "LDS ring exceeds 160 KiB");
 
     typedef typename AccOf<P>::type acc_t;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -223,15 +250,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p
     const int64_t kbytes = p.kbytes;
     const int KF = (int)(kbytes / BKB);     // full K tiles
     const bool tail = (kbytes % BKB) != 0;  // plus one partial tile
-    // Tile sequence: NPRE leading special entries (an all-zero pad that makes
-    // the count a multiple of PF, then the partial tile), then the full tiles
-    // in order. The special entries are all fetched in the prologue, so the
-    // loop body holds only unmasked loads and a single MFMA call site per
-    // stage (which keeps the 256 accumulator registers in place).
-    const int KT = (KF + (tail ? 1 : 0) + PF - 1) / PF * PF;
-    const int NPRE = KT - KF;
+    // Entry 0 is the partial tile if there is one (loaded through registers
+    // with K masking in the prologue); the full tiles follow.
+    const int KT = KF + (tail ? 1 : 0);
+    const int NPRE = tail ? 1 : 0;
 
-    const int c = tid % CPR, r0 = tid / CPR;
+    const int r0 = tid / CPR;
+    const int cg = (tid % CPR) ^ swz<CPR>(r0);   // global chunk of this lane's slot
     const uint8_t *Ab = p.A + (int64_t)row0 * p.lda_b;
     const uint8_t *Bb = p.B + (int64_t)col0 * p.ldb_b;
     const int a_rows = p.M - row0, b_rows = p.N - col0;   // >= 1
@@ -240,62 +265,49 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p
     for (int i = 0; i < A_PER_T; ++i) {
         int r = r0 + i * RS;
         r = r < a_rows ? r : a_rows - 1;   // clamped rows feed outputs never stored
-        off[i] = (uint32_t)r * (uint32_t)p.lda_b + c * 16;
+        off[i] = (uint32_t)r * (uint32_t)p.lda_b + cg * 16;
     }
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
         int r = r0 + i * RS;
         r = r < b_rows ? r : b_rows - 1;
-        off[A_PER_T + i] = (uint32_t)r * (uint32_t)p.ldb_b + c * 16;
+        off[A_PER_T + i] = (uint32_t)r * (uint32_t)p.ldb_b + cg * 16;
     }
-    const int lds0 = r0 * BKB + ((c ^ swz<CPR>(r0)) * 16);
-    // In-loop prefetches are issued unconditionally (a conditional load makes
-    // the compiler's wait counts conservative); past the last full tile they
-    // re-read it, and with no full tile at all they read the first chunk of
-    // the row, which is in bounds. The duplicate data is never consumed.
-    const int klast = KF > 0 ? KF - 1 : 0;
-    const uint32_t cdrop = KF > 0 ? 0u : (uint32_t)(c * 16);
+    // wave-uniform LDS base of this wavefront's DMA rows within a stage
+    const int wrow = wave * (64 / CPR);
 
-    auto load_fast = [&](int kt, i32x4 *R) {
+    // Entry e (> NPRE - 1) is full tile e - NPRE. Every call issues exactly
+    // NL loads (entries past the end re-read the last full tile into a stage
+    // that is free), so a fixed vmcnt tells which entry has landed. The host
+    // sends problems with no full K tile (KF == 0) to the generic kernel.
+    auto dma_entry = [&](int e) {
+        int kt = e - NPRE;
+        kt = kt < KF - 1 ? kt : KF - 1;
         const uint8_t *a = Ab + (int64_t)kt * BKB;
         const uint8_t *b = Bb + (int64_t)kt * BKB;
+        uint8_t *S = smem + (e % NS) * STAGE + wrow * BKB;
 #pragma unroll
         for (int i = 0; i < A_PER_T; ++i)
-            R[i] = *reinterpret_cast<const i32x4 *>(a + off[i]);
+            dma16(a + off[i], S + i * RS * BKB);
 #pragma unroll
         for (int i = 0; i < B_PER_T; ++i)
-            R[A_PER_T + i] = *reinterpret_cast<const i32x4 *>(b + off[A_PER_T + i]);
+            dma16(b + off[A_PER_T + i], S + BM * BKB + i * RS * BKB);
     };
-    auto load_fast_clamped = [&](int kt, i32x4 *R) {
-        const int k = kt < klast ? kt : klast;
-        const uint8_t *a = Ab + (int64_t)k * BKB;
-        const uint8_t *b = Bb + (int64_t)k * BKB;
+    // partial tile kt -> stage 0 through registers, bytes past K cleared
+    auto reg_tail = [&](int kt) {
+        const int64_t k0 = (int64_t)kt * BKB + cg * 16;
+        uint8_t *S = smem + r0 * BKB + ((tid % CPR) * 16);
 #pragma unroll
-        for (int i = 0; i < A_PER_T; ++i)
-            R[i] = *reinterpret_cast<const i32x4 *>(a + (off[i] - cdrop));
+        for (int i = 0; i < A_PER_T; ++i) {
+            const i32x4 v = load_chunk_masked(Ab + (off[i] - cg * 16), k0, kbytes, r0 + i * RS < a_rows);
+            *reinterpret_cast<i32x4 *>(S + i * RS * BKB) = v;
+        }
 #pragma unroll
-        for (int i = 0; i < B_PER_T; ++i)
-            R[A_PER_T + i] = *reinterpret_cast<const i32x4 *>(b + (off[A_PER_T + i] - cdrop));
-    };
-    auto load_tail = [&](int kt, i32x4 *R) {
-        const int64_t k0 = (int64_t)kt * BKB;
-#pragma unroll
-        for (int i = 0; i < A_PER_T; ++i)
-            R[i] = load_chunk_masked(Ab + off[i] - c * 16, k0 + c * 16, kbytes,
-                                     r0 + i * RS < a_rows);
-#pragma unroll
-        for (int i = 0; i < B_PER_T; ++i)
-            R[A_PER_T + i] = load_chunk_masked(Bb + off[A_PER_T + i] - c * 16, k0 + c * 16, kbytes,
-                                               r0 + i * RS < b_rows);
-    };
-    auto store = [&](int stage, const i32x4 *R) {
-        uint8_t *S = smem + stage * STAGE + lds0;
-#pragma unroll
-        for (int i = 0; i < A_PER_T; ++i)
-            *reinterpret_cast<i32x4 *>(S + i * RS * BKB) = R[i];
-#pragma unroll
-        for (int i = 0; i < B_PER_T; ++i)
-            *reinterpret_cast<i32x4 *>(S + BM * BKB + i * RS * BKB) = R[A_PER_T + i];
+        for (int i = 0; i < B_PER_T; ++i) {
+            const i32x4 v = load_chunk_masked(Bb + (off[A_PER_T + i] - cg * 16), k0, kbytes,
+                                              r0 + i * RS < b_rows);
+            *reinterpret_cast<i32x4 *>(S + BM * BKB + i * RS * BKB) = v;
+        }
     };
 
     acc_t acc[TM][TN];
@@ -305,55 +317,40 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p
         for (int j = 0; j < TN; ++j)
             acc[i][j] = acc_t{};
 
-    // prologue only: any entry of the sequence
-    auto load_entry = [&](int e, i32x4 *R) {
-        if (e >= NPRE) {
-            load_fast(e - NPRE, R);
-        } else if (tail && e == NPRE - 1) {
-            load_tail(KF, R);
-        } else {
-#pragma unroll
-            for (int i = 0; i < NL; ++i)
-                R[i] = i32x4{0, 0, 0, 0};
-        }
-    };
-
-    // Software pipeline. Entry t of the tile sequence is fetched from global
-    // memory into register set t % 2 two entries ahead of its use, written to
-    // LDS stage t % 2 one entry ahead, and read as fragments one k-step ahead
-    // of its MFMAs. The LDS write and the barrier that publishes the next stage
-    // sit before the last k-step's MFMAs, which then hide the barrier and the
-    // first fragment reads of the next stage. sched_barrier(0) pins this order
-    // against the compiler's scheduler.
-    i32x4 R0[NL], R1[NL];
+    // Prologue: entries 0 .. NS-2 in flight; wait for entry 0 only.
     i32x4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-    if (KT > 0) {
-        load_entry(0, R0);
-        store(0, R0);
-        load_entry(1, R1);
-    }
-    __syncthreads();
+    if (tail)
+        reg_tail(KF);
+    else
+        dma_entry(0);
+#pragma unroll
+    for (int e = 1; e < NS - 1; ++e)
+        dma_entry(e);
+    // entry 0 has landed (through LDS DMA, or through registers: lgkmcnt)
+    wait_vm_lds<(NS - 2) * NL>();
+    lds_barrier();
     read_frags<BM, BKB, TM, TN>(smem, 0, wm0, wn0, lane, fa0, fb0);
 
-    // One pipeline entry held in LDS stage `stage`; Rload receives entry
-    // kt_next from global memory, Rstore (entry + 1) goes to the other stage.
-    // Region A (before the barrier): the global loads, the fragment reads of
-    // steps 1.. and the LDS writes are interleaved one by one with the MFMAs
-    // of steps 0 .. STEPS-2 and the first KA MFMAs of the last step. Region B
-    // (after the barrier): the next stage's step-0 fragment reads interleaved
-    // with the rest of the last step's MFMAs. Each MFMA occupies the matrix
-    // pipe for several cycles, so the memory instructions issue in its shadow.
-    constexpr int NMF = TM * TN;               // MFMAs per k-step per operand pair
-    constexpr int MFI = (P == PREC_I4) ? 2 : 1; // MFMA instructions per (i, j)
-    constexpr int NFR = TM + TN;                // fragment reads per k-step
-    constexpr int KA = NMF >= 4 ? NMF / 4 : 1;  // last-step MFMAs before the barrier
-    constexpr int DSW = (NL + KA - 1) / KA;     // LDS writes per MFMA before the barrier
-    auto entry = [&](int stage, i32x4 (&Rload)[NL], int kt_next, const i32x4 (&Rstore)[NL]) {
-        const uint8_t *S = smem + stage * STAGE;
+    // One pipeline entry e in LDS stage e % NS. Region A (before the
+    // barrier): the direct-to-LDS loads of entry e + NS - 1 into the stage
+    // freed by entry e - 1; per k-step, the fragment reads of the next step
+    // and the MFMAs of this one; the first KA MFMAs of the last step. The barrier publishes entry e + 1 (its
+    // loads, issued NS - 2 entries earlier, are the oldest ones outstanding)
+    // and certifies that every wavefront has finished reading stage e % NS.
+    // Region B: step-0 fragment reads of the next stage interleaved with the
+    // rest of the last step's MFMAs.
+    constexpr int NMF = TM * TN;
+    constexpr int KA = NMF >= 4 ? NMF / 4 : 1;
+    for (int e = 0; e < KT; ++e) {
+        const uint8_t *S = smem + (e % NS) * STAGE;
+        const uint8_t *Snext = smem + ((e + 1) % NS) * STAGE;
         __builtin_amdgcn_sched_barrier(0);
-        load_fast_clamped(kt_next, Rload);
+        dma_entry(e + NS - 1);
 #pragma unroll
         for (int step = 0; step < STEPS - 1; ++step) {
+            // one scheduling region per k-step: fragment reads of the next
+            // step, then the MFMAs of this one (no back-to-back MFMAs on one
+            // accumulator across steps)
             if (step % 2 == 0) {
                 read_frags<BM, BKB, TM, TN>(S, step + 1, wm0, wn0, lane, fa1, fb1);
                 mfma_step<P, TM, TN>(fa0, fb0, acc);
@@ -361,48 +358,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p
                 read_frags<BM, BKB, TM, TN>(S, step + 1, wm0, wn0, lane, fa0, fb0);
                 mfma_step<P, TM, TN>(fa1, fb1, acc);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // STEPS is even: the last step's fragments are in buffer 1
         mfma_step<P, TM, TN, 0, KA>(fa1, fb1, acc);
-        store(stage ^ 1, Rstore);
-        // region A schedule
-#pragma unroll
-        for (int step = 0; step < STEPS - 1; ++step) {
-#pragma unroll
-            for (int f = 0; f < NMF; ++f) {
-                __builtin_amdgcn_sched_group_barrier(SG_MFMA, MFI, 0);
-                if (step == 0 && f < NL)
-                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
-                if (f < NFR)
-                    __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
-            }
-        }
-#pragma unroll
-        for (int f = 0; f < KA; ++f) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, MFI, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_DS_WR, DSW, 0);
-        }
-        __syncthreads();
-        read_frags<BM, BKB, TM, TN>(smem + (stage ^ 1) * STAGE, 0, wm0, wn0, lane, fa0, fb0);
-        mfma_step<P, TM, TN, KA, NMF>(fa1, fb1, acc);
-        // region B schedule
-#pragma unroll
-        for (int f = KA; f < NMF; ++f) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, MFI, 1);
-            if (f - KA < NFR)
-                __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 1);
-        }
         __builtin_amdgcn_sched_barrier(0);
-    };
-    for (int kt = 0; kt < KT; kt += 2) {
-        entry(0, R0, kt + 2 - NPRE, R1);   // entry kt; R1 holds entry kt + 1
-        entry(1, R1, kt + 3 - NPRE, R0);   // entry kt + 1; R0 holds entry kt + 2
+        wait_vm_lds<(NS - 2) * NL>();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags<BM, BKB, TM, TN>(Snext, 0, wm0, wn0, lane, fa0, fb0);
+        mfma_step<P, TM, TN, KA, NMF>(fa1, fb1, acc);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // the last entries' dummy loads must land before the wavefront exits
+    wait_vm_lds<0>();
     store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc);
 }
 
 // Operands without 16-byte row alignment (or with rows too long for 32-bit
-// offsets): byte-gather loads, 64-bit addressing, single prefetch.
+// offsets, or K shorter than one tile): byte-gather loads, 64-bit
+// addressing, single prefetch.
 template <int P, int BM, int BN, int BKB, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_generic_kernel(GemmProblem p,
                                                                            int tiles_m,
@@ -483,13 +457,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_generic_kernel(GemmP
 
 struct CfgShape { int BM, BN; const char *name; };
 static const CfgShape kCfg[CFG_COUNT] = {
-    {256, 256, "256x256_bk64"},
-    {128, 128, "128x128_bk64"},
-    {64, 64, "64x64_bk128"},
-    {256, 128, "256x128_bk64"},
-    {256, 256, "256x256_bk128"},
-    {128, 256, "128x256_bk64"},
-    {128, 128, "128x128_bk128"},
+    {256, 256, "256x256_bk64_ring4"},
+    {128, 128, "128x128_bk64_ring4"},
+    {64, 64, "64x64_bk128_ring3"},
+    {256, 128, "256x128_bk128_ring3"},
+    {256, 256, "256x256_bk128_ring2"},
+    {128, 256, "128x256_bk128_ring3"},
+    {128, 128, "128x128_bk128_ring4"},
+    {256, 256, "256x256_bk128_ring2_w8"},
+    {256, 256, "256x256_bk64_ring4_w8"},
+    {256, 128, "256x128_bk64_ring3_2blk"},
+    {128, 128, "128x128_bk128_ring2_2blk"},
+    {128, 256, "128x256_bk64_ring3_2blk"},
 };
 
 const char *tile_cfg_name(int cfg) {
@@ -502,9 +481,11 @@ int choose_tile_cfg(int prec, int64_t M, int64_t N, int64_t kbytes, int cu_count
     auto tiles = [&](int c) {
         return ((M + kCfg[c].BM - 1) / kCfg[c].BM) * ((N + kCfg[c].BN - 1) / kCfg[c].BN);
     };
-    // Largest tile that still gives every compute unit a workgroup.
-    if (tiles(CFG_256x256) >= cu_count)
-        return CFG_256x256;
+    // Largest tile that still gives every compute unit a workgroup (measured
+    // on MI355X: the 256x256 tile with a 128-byte K depth is the fastest once
+    // the grid fills the chip).
+    if (tiles(CFG_256x256_BK128) >= cu_count)
+        return CFG_256x256_BK128;
     if (tiles(CFG_256x128) >= cu_count)
         return CFG_256x128;
     if (tiles(CFG_128x128) >= cu_count / 2)
@@ -512,32 +493,46 @@ int choose_tile_cfg(int prec, int64_t M, int64_t N, int64_t kbytes, int cu_count
     return CFG_64x64;
 }
 
-template <int P, int BM, int BN, int BKB, int WGM, int WGN>
+template <int P>
+static hipError_t launch_generic(const GemmProblem &p, hipStream_t stream);
+
+template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS>
 static hipError_t launch_one(const GemmProblem &p, hipStream_t stream) {
+    if (p.kbytes < BKB)   // no full K tile: the ring kernel needs at least one
+        return launch_generic<P>(p, stream);
     int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
-    hipLaunchKernelGGL((gemm_tile_kernel<P, BM, BN, BKB, WGM, WGN>), grid, block, 0, stream, p,
+    hipLaunchKernelGGL((gemm_tile_kernel<P, BM, BN, BKB, WGM, WGN, NS>), grid, block, 0, stream, p,
                        tiles_m, tiles_n);
     return hipGetLastError();
 }
 
 template <int P>
+static hipError_t launch_generic(const GemmProblem &p, hipStream_t stream) {
+    constexpr int BM = 128, BN = 128;
+    int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    hipLaunchKernelGGL((gemm_tile_generic_kernel<P, BM, BN, 64, 2, 2>), dim3(tiles_m * tiles_n),
+                       dim3(256), 0, stream, p, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+template <int P>
 static hipError_t launch_prec(int cfg, const GemmProblem &p, bool aligned, hipStream_t stream) {
-    if (!aligned) {   // byte-gather loads, one shape
-        constexpr int BM = 128, BN = 128;
-        int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-        hipLaunchKernelGGL((gemm_tile_generic_kernel<P, BM, BN, 64, 2, 2>), dim3(tiles_m * tiles_n),
-                           dim3(256), 0, stream, p, tiles_m, tiles_n);
-        return hipGetLastError();
-    }
+    if (!aligned)   // byte-gather loads, one shape
+        return launch_generic<P>(p, stream);
     switch (cfg) {
-    case CFG_256x256: return launch_one<P, 256, 256, 64, 2, 2>(p, stream);
-    case CFG_128x128: return launch_one<P, 128, 128, 64, 2, 2>(p, stream);
-    case CFG_64x64: return launch_one<P, 64, 64, 128, 2, 2>(p, stream);
-    case CFG_256x128: return launch_one<P, 256, 128, 64, 2, 2>(p, stream);
-    case CFG_256x256_BK128: return launch_one<P, 256, 256, 128, 2, 2>(p, stream);
-    case CFG_128x256: return launch_one<P, 128, 256, 64, 2, 2>(p, stream);
-    case CFG_128x128_BK128: return launch_one<P, 128, 128, 128, 2, 2>(p, stream);
+    case CFG_256x256: return launch_one<P, 256, 256, 64, 2, 2, 4>(p, stream);
+    case CFG_128x128: return launch_one<P, 128, 128, 64, 2, 2, 4>(p, stream);
+    case CFG_64x64: return launch_one<P, 64, 64, 128, 2, 2, 3>(p, stream);
+    case CFG_256x128: return launch_one<P, 256, 128, 128, 2, 2, 3>(p, stream);
+    case CFG_256x256_BK128: return launch_one<P, 256, 256, 128, 2, 2, 2>(p, stream);
+    case CFG_128x256: return launch_one<P, 128, 256, 128, 2, 2, 3>(p, stream);
+    case CFG_128x128_BK128: return launch_one<P, 128, 128, 128, 2, 2, 4>(p, stream);
+    case CFG_256x256_W8: return launch_one<P, 256, 256, 128, 4, 2, 2>(p, stream);
+    case CFG_256x256_W8_BK64: return launch_one<P, 256, 256, 64, 4, 2, 4>(p, stream);
+    case CFG_256x128_2B: return launch_one<P, 256, 128, 64, 2, 2, 3>(p, stream);
+    case CFG_128x128_2B: return launch_one<P, 128, 128, 128, 2, 2, 2>(p, stream);
+    case CFG_128x256_2B: return launch_one<P, 128, 256, 64, 2, 2, 3>(p, stream);
     default: return hipErrorInvalidValue;
     }
 }

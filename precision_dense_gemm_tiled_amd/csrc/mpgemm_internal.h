@@ -24,13 +24,18 @@ struct GemmProblem {
 // Tile configurations of the square/rectangular tile kernel. The index is
 // stable (it names the configuration in profiles and the ablation override).
 enum TileCfg {
-    CFG_256x256 = 0,        // 4 waves of 128x128, BK = 64 bytes of K per stage
-    CFG_128x128 = 1,        // 4 waves of 64x64,   BK = 64 B
-    CFG_64x64 = 2,          // 4 waves of 32x32,   BK = 128 B
-    CFG_256x128 = 3,        // 4 waves of 128x64,  BK = 64 B
-    CFG_256x256_BK128 = 4,  // K depth ablation of the 256x256 tile
-    CFG_128x256 = 5,        // 4 waves of 64x128,  BK = 64 B
-    CFG_128x128_BK128 = 6,  // K depth ablation of the 128x128 tile
+    CFG_256x256 = 0,        // 4 waves of 128x128, BK = 64 bytes of K, 4-stage LDS ring
+    CFG_128x128 = 1,        // 4 waves of 64x64,   BK = 64 B,  4 stages
+    CFG_64x64 = 2,          // 4 waves of 32x32,   BK = 128 B, 3 stages
+    CFG_256x128 = 3,        // 4 waves of 128x64,  BK = 128 B, 3 stages
+    CFG_256x256_BK128 = 4,  // 4 waves of 128x128, BK = 128 B, 2 stages
+    CFG_128x256 = 5,        // 4 waves of 64x128,  BK = 128 B, 3 stages
+    CFG_128x128_BK128 = 6,  // 4 waves of 64x64,   BK = 128 B, 4 stages
+    CFG_256x256_W8 = 7,     // 8 waves of 64x128,  BK = 128 B, 2 stages
+    CFG_256x256_W8_BK64 = 8,// 8 waves of 64x128,  BK = 64 B,  4 stages
+    CFG_256x128_2B = 9,     // 4 waves of 128x64, BK = 64 B, 3 stages: 72 KiB, two blocks per CU
+    CFG_128x128_2B = 10,    // 4 waves of 64x64, BK = 128 B, 2 stages: 64 KiB, two blocks per CU
+    CFG_128x256_2B = 11,    // 4 waves of 64x128, BK = 64 B, 3 stages: 72 KiB, two blocks per CU
     CFG_COUNT
 };
 

@@ -69,7 +69,7 @@ def test_every_tile_config(prec, monkeypatch):
     M, N, K = 300, 520, 200
     A, B = inputs.gemm_problem(prec, M, N, K, seed=77)
     ref = _ref(prec, A, B, K)
-    for cfg in range(7):
+    for cfg in range(12):
         monkeypatch.setenv("MPGEMM_TILE_CFG", str(cfg))
         with mp.Handle() as h:
             a, b = dev(A), dev(B)
