@@ -488,8 +488,8 @@ int choose_tile_cfg(int prec, int64_t M, int64_t N, int64_t kbytes, int cu_count
         return CFG_256x256_BK128;
     if (tiles(CFG_256x128) >= cu_count)
         return CFG_256x128;
-    if (tiles(CFG_128x128) >= cu_count / 2)
-        return CFG_128x128;
+    if (tiles(CFG_128x128_BK128) >= cu_count / 2)
+        return CFG_128x128_BK128;
     return CFG_64x64;
 }
 
