@@ -16,6 +16,7 @@ struct mpgemm_ctx {
     int device;
     int cu_count;
     int forced_tile_cfg;   // -1: heuristic; else a TileCfg index (MPGEMM_TILE_CFG)
+    int forced_w4a16_cfg;  // -1: heuristic; else a W4A16Cfg index (MPGEMM_W4A16_CFG)
 };
 
 namespace {
@@ -122,6 +123,12 @@ mpgemm_status_t mpgemm_create(mpgemm_handle_t *out, int device) {
         if (v >= 0 && v < mpg::CFG_COUNT)
             h->forced_tile_cfg = v;
     }
+    h->forced_w4a16_cfg = -1;
+    if (const char *env = std::getenv("MPGEMM_W4A16_CFG")) {
+        int v = std::atoi(env);
+        if (v >= 0 && v < mpg::W4A16_CFG_COUNT)
+            h->forced_w4a16_cfg = v;
+    }
     *out = h;
     return MPGEMM_OK;
 }
@@ -222,7 +229,8 @@ mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_
     p.N = (int)N;
     p.K = (int)K;
     p.G = K > 0 ? (int)group_size : 32;
-    hipError_t e = mpg::launch_w4a16(p, static_cast<hipStream_t>(stream));
+    int cfg = h->forced_w4a16_cfg >= 0 ? h->forced_w4a16_cfg : mpg::choose_w4a16_cfg(M, N, K);
+    hipError_t e = mpg::launch_w4a16(p, cfg, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
 }
 

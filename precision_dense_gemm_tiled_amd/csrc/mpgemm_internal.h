@@ -53,6 +53,21 @@ struct W4A16Problem {
     int M, N, K, G;
 };
 
-hipError_t launch_w4a16(const W4A16Problem &p, hipStream_t stream);
+// Kernel configurations of the weight-only path (index stable, as for TileCfg).
+enum W4A16Cfg {
+    W4A16_MFMA_DECODE = 0,  // 16x16x32 MFMA, 16 weight rows per workgroup, K split over 4 wavefronts
+    W4A16_MFMA_TILE = 1,    // 16x16x32 MFMA, 32 x 64 output tiles
+    W4A16_GEMV_R1_KS2 = 2,  // VALU GEMV, 1 weight row per wavefront, K split over 2 wavefronts
+    W4A16_GEMV_R2_KS2 = 3,
+    W4A16_GEMV_R4_KS2 = 4,
+    W4A16_GEMV_R2_KS1 = 5,  // ... whole K per wavefront
+    W4A16_GEMV_R4_KS1 = 6,
+    W4A16_GEMV_R8_KS1 = 7,
+    W4A16_CFG_COUNT
+};
+
+const char *w4a16_cfg_name(int cfg);
+int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K);
+hipError_t launch_w4a16(const W4A16Problem &p, int cfg, hipStream_t stream);
 
 }  // namespace mpg

@@ -250,6 +250,34 @@ def test_w4a16_ragged(M, N, K, G):
     _check_w4(X, W, S, K, G, f"w4a16 {M}x{N}x{K} G={G}")
 
 
+W4A16_CFGS = 8
+
+
+def test_w4a16_every_config(monkeypatch):
+    """Each weight-only kernel configuration (forced through the ablation
+    override) on ragged shapes, group sizes 32 ... 256 and the decode layer,
+    plus the bit-exact small-integer case."""
+    shapes = [(1, 4096, 4096, 128), (1, 50, 96, 32), (2, 70, 512, 64), (3, 33, 256, 128),
+              (5, 130, 1024, 256), (17, 40, 4096, 4096)]
+    problems = [(shape, inputs.w4a16_problem(*shape, seed=sum(shape) + 7)) for shape in shapes]
+    refs = [oracle.gemm_w4a16(X, W, S, shape[2], shape[3], want_t2=True) for shape, (X, W, S) in problems]
+    r = np.random.default_rng(5)
+    Xi = r.integers(-4, 5, (3, 2048)).astype(np.float16)
+    Wi = r.integers(0, 256, (96, 1024)).astype(np.uint8)
+    Si = (2.0 ** -r.integers(3, 9, (96, 2048 // 64))).astype(np.float16)
+    yi = oracle.f16_encode_rne_array(oracle.gemm_w4a16(Xi, Wi, Si, 2048, 64))
+    for cfg in range(W4A16_CFGS):
+        monkeypatch.setenv("MPGEMM_W4A16_CFG", str(cfg))
+        with mp.Handle() as h:
+            for ((M, N, K, G), (X, W, S)), (y, t2) in zip(problems, refs):
+                got = host(mp.gemm_w4a16(dev(X), dev(W), dev(S), G, handle=h.value))
+                err = np.abs(got.astype(np.float64) - y)
+                bad = np.argwhere(err > w4a16_tol(y, t2, K))
+                assert bad.size == 0, f"cfg {cfg} {M}x{N}x{K} G={G}: {len(bad)} outside the bar"
+            got = host(mp.gemm_w4a16(dev(Xi), dev(Wi), dev(Si), 64, handle=h.value)).view(np.uint16)
+            assert np.array_equal(got, yi), f"cfg {cfg}: small-integer case not bit-exact"
+
+
 @pytest.mark.parametrize("G", [32, 128])
 def test_w4a16_one_hot_exact(G):
     """x = e_k: y[n] = rne16(q[n,k] * s[n, k/G]) exactly (a single nonzero term)."""
