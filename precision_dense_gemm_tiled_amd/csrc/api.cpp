@@ -17,6 +17,7 @@ struct mpgemm_ctx {
     int cu_count;
     int forced_tile_cfg;   // -1: heuristic; else a TileCfg index (MPGEMM_TILE_CFG)
     int forced_w4a16_cfg;  // -1: heuristic; else a W4A16Cfg index (MPGEMM_W4A16_CFG)
+    mpg::W4A16Workspace ws; // split-K fp32 partial sums of the weight-only path (device memory)
 };
 
 namespace {
@@ -57,6 +58,9 @@ mpgemm_status_t check_gemm(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K, c
         return MPGEMM_ERR_INVALID_ARG;
     return MPGEMM_OK;
 }
+
+// Split-K workspace per handle: 32 MiB of fp32 partial sums.
+constexpr int64_t kSplitPartialFloats = int64_t(8) << 20;
 
 mpgemm_status_t bind_device(mpgemm_handle_t h) {
     int cur = -1;
@@ -129,11 +133,33 @@ mpgemm_status_t mpgemm_create(mpgemm_handle_t *out, int device) {
         if (v >= 0 && v < mpg::W4A16_CFG_COUNT)
             h->forced_w4a16_cfg = v;
     }
+    // Split-K workspace of the weight-only path (fp32 K slices of Y),
+    // allocated once here.
+    h->ws.partial = nullptr;
+    h->ws.partial_floats = kSplitPartialFloats;
+    int prev = -1;
+    bool ok = hipGetDevice(&prev) == hipSuccess && hipSetDevice(device) == hipSuccess;
+    ok = ok && hipMalloc(reinterpret_cast<void **>(&h->ws.partial), kSplitPartialFloats * sizeof(float)) == hipSuccess;
+    if (prev >= 0)
+        (void)hipSetDevice(prev);
+    if (!ok) {
+        mpgemm_destroy(h);
+        return MPGEMM_ERR_HIP;
+    }
     *out = h;
     return MPGEMM_OK;
 }
 
 mpgemm_status_t mpgemm_destroy(mpgemm_handle_t h) {
+    if (!h)
+        return MPGEMM_OK;
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(h->device);
+    if (h->ws.partial)
+        (void)hipFree(h->ws.partial);
+    if (prev >= 0)
+        (void)hipSetDevice(prev);
     delete h;
     return MPGEMM_OK;
 }
@@ -230,7 +256,7 @@ mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_
     p.K = (int)K;
     p.G = K > 0 ? (int)group_size : 32;
     int cfg = h->forced_w4a16_cfg >= 0 ? h->forced_w4a16_cfg : mpg::choose_w4a16_cfg(M, N, K);
-    hipError_t e = mpg::launch_w4a16(p, cfg, static_cast<hipStream_t>(stream));
+    hipError_t e = mpg::launch_w4a16(p, cfg, h->ws, h->cu_count, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
 }
 

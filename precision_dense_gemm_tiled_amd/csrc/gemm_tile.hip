@@ -22,6 +22,7 @@
 // the order in which k values reach the MFMA is the same on both sides and
 // the dot product is unchanged.
 #include "mpgemm_internal.h"
+#include "lds_dma.h"
 
 namespace mpg {
 
@@ -180,30 +181,6 @@ __device__ __forceinline__ void store_tile(const GemmProblem &p, int row0, int c
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).
 // The LDS destination is wave-uniform: lane l writes lds + 16 * l.
-__device__ __forceinline__ void dma16(const uint8_t *g, uint8_t *lds) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                     (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
-}
-
-// s_waitcnt immediate for "at most VM vector-memory operations outstanding,
-// all LDS operations done" (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
-// expcnt 6:4 left at its maximum, lgkmcnt 11:8).
-template <int VM>
-__device__ __forceinline__ void wait_vm_lds() {
-    static_assert(VM >= 0 && VM < 64, "vmcnt range");
-    constexpr int imm = (VM & 15) | ((VM >> 4) << 14) | (7 << 4);
-    __builtin_amdgcn_s_waitcnt(imm);
-}
-
-// Workgroup barrier that publishes LDS-DMA data without waiting for every
-// outstanding load: the caller's wait_vm_lds<> decides which loads must have
-// landed. Compiler-level fences keep memory operations on their side.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // Main kernel for 16-byte aligned operands whose BM (BN) rows span less than
 // 2^31 bytes. Full K tiles move from global memory straight into an NS-stage
 // LDS ring with direct-to-LDS loads (no staging registers, no ds_write),

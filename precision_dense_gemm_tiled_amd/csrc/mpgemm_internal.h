@@ -63,11 +63,27 @@ enum W4A16Cfg {
     W4A16_GEMV_R2_KS1 = 5,  // ... whole K per wavefront
     W4A16_GEMV_R4_KS1 = 6,
     W4A16_GEMV_R8_KS1 = 7,
+    W4A16_SLICE_16x16_K4 = 8,  // MFMA, activations resident in LDS, 16 x 16 tile, K over 4 wavefronts
+    W4A16_SLICE_32x32_K2 = 9,  // ... 32 x 32 tile, 2 column x 2 K wavefronts
+    W4A16_SLICE_64x128 = 10,   // ... 64 x 128 tile
+    W4A16_SLICE_128x128 = 11,  // ... 128 x 128 tile
     W4A16_CFG_COUNT
+};
+
+// Split-K workspace owned by a handle: the fp32 K slices of Y.
+struct W4A16Workspace {
+    float *partial;
+    int64_t partial_floats;
+};
+
+struct W4A16Split {
+    float *partial;
+    int ks, kslice, mblocks, ngroups;
 };
 
 const char *w4a16_cfg_name(int cfg);
 int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K);
-hipError_t launch_w4a16(const W4A16Problem &p, int cfg, hipStream_t stream);
+hipError_t launch_w4a16(const W4A16Problem &p, int cfg, const W4A16Workspace &ws, int cu_count,
+                        hipStream_t stream);
 
 }  // namespace mpg

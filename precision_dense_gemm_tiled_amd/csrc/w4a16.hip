@@ -21,6 +21,10 @@
 // MFMAs sum x*q exactly in fp32 and the group scale multiplies that sum
 // (fp32). Otherwise the scale multiplies the fp16 weights before the MFMA.
 #include "mpgemm_internal.h"
+#include "lds_dma.h"
+
+#include <algorithm>
+#include <climits>
 
 namespace mpg {
 
@@ -356,6 +360,201 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(W4A16Problem p, int lg)
     }
 }
 
+// ---------------------------------------------------------------- slice MFMA path
+//
+// Mid-size and prefill M. The weights dominate the bytes and the activations
+// are reused by every output column, so a workgroup keeps the activations of
+// its K range (BM rows) resident in LDS, loaded once with coalesced
+// direct-to-LDS loads into rows whose 16-byte chunks are XOR-swizzled by
+// row & 15 (the 16 rows of a fragment read fall in distinct banks). Its
+// wavefronts stream their weight rows straight into registers, every weight
+// load issued before the first product, dequantise them exactly, multiply by
+// the group scale in fp16 and feed v_mfma_f32_16x16x32_f16 (the
+// fused-int4-gemm-sm75 README dequantises to fp16 in registers before the
+// matrix product).
+//
+// Dequantisation in natural k order, so the activations need no reordering:
+// with u = nibble ^ 8 = q + 8, broadcasting byte b of u to all four bytes puts
+// nibble 2b in bits 0..3 and nibble 2b+1 in bits 20..23; one mask-or with the
+// fp16 patterns 0x6400 (1024, unit step) and 0x5400 (64, step 1/16) gives the
+// pair (1024 + u_2b, 64 + u_2b+1), and subtracting (1032, 72) gives q exactly.
+//
+// The 4 wavefronts are arranged WN (columns) x WK (K quarters); the WK
+// partial sums meet in LDS. When the grid still has too few workgroups, K is
+// also split over KS workgroups: each writes its fp32 slice of Y to the
+// workspace and a second kernel adds the slices in slice order.
+
+__device__ __forceinline__ f16x8 dequant8_natural(uint32_t w, _Float16 scale) {
+    const uint32_t u = w ^ 0x88888888u;
+    const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-72.0f};
+    const f16x2 s2 = {scale, scale};
+    f16x2 q[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t bb = __builtin_amdgcn_perm(u, u, 0x01010101u * (uint32_t)b);
+        q[b] = (__builtin_bit_cast(f16x2, (bb & 0x00F0000Fu) | 0x54006400u) + bias) * s2;
+    }
+    return f16x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+}
+
+template <int MB, int NB, int WN, int WK, int NST>
+__global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16Split sk, int lg) {
+    static_assert(WN * WK == 4, "4 wavefronts");
+    constexpr int BM = 16 * MB, BN = 16 * NB * WN;
+    constexpr int CPROW = 16 * NST * WK;        // 16-byte chunks per LDS row (the workgroup's K range)
+    constexpr int UPR = CPROW / 64;             // 1 KiB direct-to-LDS units per row
+    constexpr int UNITS = BM * UPR;
+    constexpr int NW = NST * NB * 2;            // weight + scale loads per thread
+    static_assert(CPROW % 64 == 0 && UNITS % 4 == 0 && NW < 64, "slice shape");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+    const int wn = wave % WN, wk = wave / WN;
+
+    // Workgroup -> (column group, row block, K slice). Consecutive workgroup
+    // ids go round-robin over the 8 XCDs; give each XCD a contiguous range so
+    // the K slices and row blocks of one column group share an L2.
+    int logical = blockIdx.x;
+    {
+        const int nblk = gridDim.x;
+        if (nblk >= 8) {
+            const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+            const int base = nblk / 8, rem = nblk % 8;
+            logical = xcd * base + (xcd < rem ? xcd : rem) + local;
+        }
+    }
+    const int ks = logical % sk.ks;
+    const int tile = logical / sk.ks;          // = ng * mblocks + mb
+    const int mb = tile % sk.mblocks, ng = tile / sk.mblocks;
+    const int m0 = mb * BM;
+    const int k_begin = ks * sk.kslice;
+    const int k_end = min(p.K, k_begin + sk.kslice);
+    const int kw = k_begin + wk * 128 * NST;    // this wavefront's K range starts here
+    const int n0w = ng * BN + wn * 16 * NB;
+
+    // 1. activation rows of the workgroup's K range -> LDS (clamped addresses:
+    //    rows past M and k past the range only meet zero weights or outputs
+    //    that are never stored)
+    __shared__ __attribute__((aligned(16))) uint8_t xs[BM * CPROW * 16];
+#pragma unroll
+    for (int v = 0; v < UNITS / 4; ++v) {
+        const int u = wave + 4 * v, r = u / UPR, p0 = (u % UPR) * 64;
+        const int c = (p0 + lane) ^ (r & 15);
+        const int k = min(k_begin + 8 * c, p.K - 8);
+        const uint16_t *src = p.X + (int64_t)min(m0 + r, p.M - 1) * p.ldx + k;
+        dma16(src, xs + (r * CPROW + p0) * 16);
+    }
+    // the weight loads below must stay behind the direct-to-LDS loads: the
+    // wait before the first fragment read counts on the NW youngest loads
+    // being theirs
+    asm volatile("" ::: "memory");
+
+    // 2. every weight word and scale of this wavefront's K range -> registers
+    const uint8_t *wrow[NB];
+    const uint16_t *srow[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int n = min(n0w + 16 * j + (lane & 15), p.N - 1);
+        wrow[j] = p.W + (int64_t)n * p.ldw_b;
+        srow[j] = p.S + (int64_t)n * p.lds;
+    }
+    i32x4 wr[NST][NB];
+    uint16_t sr[NST][NB];
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
+        int k = kw + 128 * s + 32 * g;
+        k = k + 32 <= p.K ? k : p.K - 32;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            wr[s][j] = *reinterpret_cast<const i32x4 *>(wrow[j] + (k >> 1));
+            sr[s][j] = srow[j][k >> lg];
+        }
+    }
+    wait_vm_lds<NW>();
+    lds_barrier();
+
+    // 3. products, no barrier: the weights of step s arrive in issue order
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const i32x4 *xq = reinterpret_cast<const i32x4 *>(xs);
+#pragma unroll
+    for (int s = 0; s < NST; ++s) {
+        if (kw + 128 * s >= k_end)
+            break;
+        const bool live = kw + 128 * s + 32 * g < k_end;
+        const int cs = 16 * (wk * NST + s);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f16x8 a[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                a[i] = __builtin_bit_cast(f16x8, xq[(16 * i + (lane & 15)) * CPROW + cs + ((4 * g + t) ^ (lane & 15))]);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                // a run past the K range gets q = 0 (u = 8 in every nibble)
+                const uint32_t w = live ? (uint32_t)wr[s][j][t] : 0u;
+                const f16x8 b = dequant8_natural(w, __builtin_bit_cast(_Float16, sr[s][j]));
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b, acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+
+    // 4. add the WK partial sums through LDS (reusing the activation buffer)
+    if constexpr (WK > 1) {
+        static_assert(BM * CPROW * 16 >= 4 * MB * NB * 4 * 64 * 4, "reduction buffer");
+        __syncthreads();
+        f32x4 *red = reinterpret_cast<f32x4 *>(xs);
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                red[((wave * MB + i) * NB + j) * 64 + lane] = acc[i][j];
+        __syncthreads();
+        if (wk != 0)
+            return;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int o = 1; o < WK; ++o)
+                    acc[i][j] += red[(((o * WN + wn) * MB + i) * NB + j) * 64 + lane];
+    }
+
+    // 5. store: Y directly, or this K slice's fp32 part of Y
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * i + 4 * g + r, n = n0w + 16 * j + (lane & 15);
+                if (m < p.M && n < p.N) {
+                    if (sk.ks == 1)
+                        p.Y[(int64_t)m * p.ldy + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
+                    else
+                        sk.partial[((int64_t)ks * p.M + m) * p.N + n] = acc[i][j][r];
+                }
+            }
+}
+
+// Y = fp16(sum of the KS fp32 slices), slices added in slice order.
+__global__ __launch_bounds__(256) void w4a16_reduce_kernel(W4A16Problem p, const float *partial, int ks) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)p.M * p.N;
+    if (e >= total)
+        return;
+    float y = 0.f;
+    for (int o = 0; o < ks; ++o)
+        y += partial[o * total + e];
+    const int64_t m = e / p.N, n = e - m * p.N;
+    p.Y[m * p.ldy + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
+}
+
 template <int MT, int WN, int WK, int U>
 static hipError_t launch_cfg(const W4A16Problem &p, hipStream_t stream, int lg) {
     dim3 block(64 * WN * WK);
@@ -387,30 +586,67 @@ static hipError_t launch_gemv(const W4A16Problem &p, hipStream_t stream, int lg)
     return launch_gemv_mm<R, KS, 4>(p, stream, lg);
 }
 
+template <int MB, int NB, int WN, int WK, int NST>
+static hipError_t launch_slice(const W4A16Problem &p, const W4A16Workspace &ws, int cu_count,
+                               hipStream_t stream, int lg) {
+    constexpr int BM = 16 * MB, BN = 16 * NB * WN, KSPAN = 128 * NST * WK;
+    W4A16Split sk;
+    sk.mblocks = (p.M + BM - 1) / BM;
+    sk.ngroups = (p.N + BN - 1) / BN;
+    const int64_t tiles = (int64_t)sk.mblocks * sk.ngroups;
+    // K slices: at least K / KSPAN (what one workgroup holds), more while the
+    // grid would leave compute units idle
+    int ks = (p.K + KSPAN - 1) / KSPAN;
+    while (tiles * ks < cu_count && (int64_t)(ks + 1) * 128 <= p.K)
+        ++ks;
+    // equal slices in whole 128-k steps
+    const int steps = (p.K + 127) / 128;
+    const int spk = (steps + ks - 1) / ks;
+    ks = (steps + spk - 1) / spk;
+    if (ks > 1 && (int64_t)ks * p.M * p.N > ws.partial_floats)
+        return hipErrorOutOfMemory;   // caller falls back to a configuration without a workspace
+    sk.ks = ks;
+    sk.kslice = 128 * spk;
+    sk.partial = ws.partial;
+    const int64_t blocks = tiles * ks;
+    if (blocks > INT_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((w4a16_slice_kernel<MB, NB, WN, WK, NST>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       p, sk, lg);
+    if (ks == 1)
+        return hipGetLastError();
+    const int64_t total = (int64_t)p.M * p.N;
+    hipLaunchKernelGGL(w4a16_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p,
+                       (const float *)ws.partial, ks);
+    return hipGetLastError();
+}
+
 const char *w4a16_cfg_name(int cfg) {
     static const char *names[W4A16_CFG_COUNT] = {
         "mfma 16 rows x 16 cols, K split 4", "mfma 32 x 64 tile",
-        "gemv R1 KS2", "gemv R2 KS2", "gemv R4 KS2", "gemv R2 KS1", "gemv R4 KS1", "gemv R8 KS1"};
+        "gemv R1 KS2", "gemv R2 KS2", "gemv R4 KS2", "gemv R2 KS1", "gemv R4 KS1", "gemv R8 KS1",
+        "slice 16 x 16, K over 4 wavefronts", "slice 32 x 32, K over 2 wavefronts",
+        "slice 64 x 128", "slice 128 x 128"};
     return cfg >= 0 && cfg < W4A16_CFG_COUNT ? names[cfg] : "?";
 }
 
 int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K) {
     (void)N;
     (void)K;
-    // measured at N = K = 4096 (cold weights): the GEMV wins up to M = 4
+    // measured at N = K = 4096 (cold weights)
     if (M == 1)
         return W4A16_GEMV_R2_KS2;
     if (M <= 4)
         return W4A16_GEMV_R4_KS2;
     if (M <= 16)
-        return W4A16_MFMA_DECODE;
-    return W4A16_MFMA_TILE;
+        return W4A16_SLICE_16x16_K4;
+    if (M <= 64)
+        return W4A16_SLICE_32x32_K2;
+    return W4A16_SLICE_64x128;
 }
 
-hipError_t launch_w4a16(const W4A16Problem &p, int cfg, hipStream_t stream) {
-    int lg = 0;
-    while ((1 << lg) < p.G)
-        ++lg;
+static hipError_t launch_one(const W4A16Problem &p, int cfg, const W4A16Workspace &ws, int cu_count,
+                             hipStream_t stream, int lg) {
     switch (cfg) {
     case W4A16_MFMA_DECODE: return launch_cfg<1, 1, 4, 8>(p, stream, lg);
     case W4A16_MFMA_TILE: return launch_cfg<2, 4, 1, 2>(p, stream, lg);
@@ -420,8 +656,25 @@ hipError_t launch_w4a16(const W4A16Problem &p, int cfg, hipStream_t stream) {
     case W4A16_GEMV_R2_KS1: return launch_gemv<2, 1>(p, stream, lg);
     case W4A16_GEMV_R4_KS1: return launch_gemv<4, 1>(p, stream, lg);
     case W4A16_GEMV_R8_KS1: return launch_gemv<8, 1>(p, stream, lg);
+    case W4A16_SLICE_16x16_K4: return launch_slice<1, 1, 1, 4, 8>(p, ws, cu_count, stream, lg);
+    case W4A16_SLICE_32x32_K2: return launch_slice<2, 1, 2, 2, 8>(p, ws, cu_count, stream, lg);
+    case W4A16_SLICE_64x128: return launch_slice<4, 2, 4, 1, 8>(p, ws, cu_count, stream, lg);
+    case W4A16_SLICE_128x128: return launch_slice<8, 2, 4, 1, 4>(p, ws, cu_count, stream, lg);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_w4a16(const W4A16Problem &p, int cfg, const W4A16Workspace &ws, int cu_count,
+                        hipStream_t stream) {
+    int lg = 0;
+    while ((1 << lg) < p.G)
+        ++lg;
+    if (p.K == 0)   // Y = 0: the GEMV writes zeros without touching the operands
+        cfg = W4A16_GEMV_R2_KS2;
+    hipError_t e = launch_one(p, cfg, ws, cu_count, stream, lg);
+    if (e == hipErrorOutOfMemory)   // split-K workspace too small for this shape
+        e = launch_one(p, p.M <= 16 ? W4A16_MFMA_DECODE : W4A16_MFMA_TILE, ws, cu_count, stream, lg);
+    return e;
 }
 
 }  // namespace mpg

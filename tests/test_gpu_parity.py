@@ -250,7 +250,7 @@ def test_w4a16_ragged(M, N, K, G):
     _check_w4(X, W, S, K, G, f"w4a16 {M}x{N}x{K} G={G}")
 
 
-W4A16_CFGS = 8
+W4A16_CFGS = 12
 
 
 def test_w4a16_every_config(monkeypatch):
@@ -258,7 +258,8 @@ def test_w4a16_every_config(monkeypatch):
     override) on ragged shapes, group sizes 32 ... 256 and the decode layer,
     plus the bit-exact small-integer case."""
     shapes = [(1, 4096, 4096, 128), (1, 50, 96, 32), (2, 70, 512, 64), (3, 33, 256, 128),
-              (5, 130, 1024, 256), (17, 40, 4096, 4096)]
+              (5, 130, 1024, 256), (17, 40, 4096, 4096), (16, 4096, 4096, 128), (128, 1000, 4096, 128),
+              (40, 200, 1440, 32), (130, 70, 640, 128)]
     problems = [(shape, inputs.w4a16_problem(*shape, seed=sum(shape) + 7)) for shape in shapes]
     refs = [oracle.gemm_w4a16(X, W, S, shape[2], shape[3], want_t2=True) for shape, (X, W, S) in problems]
     r = np.random.default_rng(5)
@@ -270,12 +271,22 @@ def test_w4a16_every_config(monkeypatch):
         monkeypatch.setenv("MPGEMM_W4A16_CFG", str(cfg))
         with mp.Handle() as h:
             for ((M, N, K, G), (X, W, S)), (y, t2) in zip(problems, refs):
-                got = host(mp.gemm_w4a16(dev(X), dev(W), dev(S), G, handle=h.value))
+                xd, wd, sd = dev(X), dev(W), dev(S)
+                got = host(mp.gemm_w4a16(xd, wd, sd, G, handle=h.value))
                 err = np.abs(got.astype(np.float64) - y)
                 bad = np.argwhere(err > w4a16_tol(y, t2, K))
                 assert bad.size == 0, f"cfg {cfg} {M}x{N}x{K} G={G}: {len(bad)} outside the bar"
+                # reproducible: the same call gives the same bits (split-K adds slices in a fixed order)
+                again = host(mp.gemm_w4a16(xd, wd, sd, G, handle=h.value))
+                assert np.array_equal(got.view(np.uint16), again.view(np.uint16)), f"cfg {cfg} {M}x{N}x{K}: not reproducible"
             got = host(mp.gemm_w4a16(dev(Xi), dev(Wi), dev(Si), 64, handle=h.value)).view(np.uint16)
             assert np.array_equal(got, yi), f"cfg {cfg}: small-integer case not bit-exact"
+            # twice in a row: the split-K arrival counters must be back at zero
+            got = host(mp.gemm_w4a16(dev(Xi), dev(Wi), dev(Si), 64, handle=h.value)).view(np.uint16)
+            assert np.array_equal(got, yi), f"cfg {cfg}: second call differs"
+            z = mp.gemm_w4a16(dev(np.zeros((3, 0), np.float16)), dev(np.zeros((5, 0), np.uint8)),
+                              dev(np.zeros((5, 0), np.float16)), 32, handle=h.value)
+            assert np.array_equal(host(z).astype(np.float64), np.zeros((3, 5))), f"cfg {cfg}: K = 0"
 
 
 @pytest.mark.parametrize("G", [32, 128])
