@@ -44,8 +44,13 @@
  *    boundary; such a read never crosses into another page.
  *  - Argument errors return before any HIP call and leave outputs untouched.
  *  - Output rows may not overlap inputs.
- *  - A handle is immutable after creation; calls on different streams may run
- *    concurrently with one handle.
+ *  - A handle owns 32 MiB of device memory, allocated by mpgemm_create and
+ *    freed by mpgemm_destroy: the workspace where mpgemm_run_w4a16 keeps the
+ *    fp32 partial sums of a K split. No call allocates memory.
+ *  - mpgemm_run_{f16,i8,i4} calls may run concurrently on different streams
+ *    with one handle. mpgemm_run_w4a16 calls that share a handle must not
+ *    overlap in time (issue them on one stream, or use one handle per stream):
+ *    they share its workspace.
  */
 #ifndef MPGEMM_H
 #define MPGEMM_H
@@ -67,7 +72,8 @@ typedef enum {
 } mpgemm_status_t;
 
 /* Create a handle bound to `device` (device < 0: the current device). Checks
- * that the device exists and is gfx950; caches its compute-unit count. */
+ * that the device exists and is gfx950, caches its compute-unit count and
+ * allocates the handle's workspace (MPGEMM_ERR_HIP if that fails). */
 mpgemm_status_t mpgemm_create(mpgemm_handle_t *out, int device);
 
 /* Destroy a handle. NULL is accepted (no-op). */
