@@ -205,7 +205,7 @@ def time_graph(prob, launches, replays):
     return start.elapsed_time(stop) / 1e3 / (replays * launches)
 
 
-def sweep_entry(prec, M, N, K, seed, steps, warmup):
+def sweep_entry(prec, M, N, K, seed, steps, warmup, eager=False):
     copies = copies_for_cold(prec, M, N, K)
     p = Problem(prec, M, N, K, seed, copies)
     # expected kernel time at ~30% of the roofline sets the launches per graph
@@ -213,8 +213,14 @@ def sweep_entry(prec, M, N, K, seed, steps, warmup):
                 algorithmic_bytes(prec, M, N, K) / (HBM_GBS * 1e9 * 0.3))
     launches = int(min(max(len(p.ins), 0.02 / max(est_s, 1e-7)), 2048))
     launches = max(launches, 2)
-    t = time_graph(p, launches, max(steps, 3))
-    reps = launches * max(steps, 3)
+    if eager:
+        # one launch at a time (for counter collection, which does not follow
+        # graph replays); launch overhead is included
+        reps = launches * max(steps, 3)
+        t = time_launches(p.launch, reps, max(warmup, 1))
+    else:
+        t = time_graph(p, launches, max(steps, 3))
+        reps = launches * max(steps, 3)
     rf = roofline(prec, M, N, K, t)
     del p
     import torch
@@ -224,7 +230,8 @@ def sweep_entry(prec, M, N, K, seed, steps, warmup):
             "throughput": round(2.0 * M * N * K / t / 1e12, 3), "unit": unit,
             "roofline_bound": rf["bound"], "roofline_frac": rf["frac"],
             "hbm_GBps_algorithmic": round(algorithmic_bytes(prec, M, N, K) / t / 1e9, 1),
-            "input_copies": copies, "launches": reps, "timing": "hip graph replay"}
+            "input_copies": copies, "launches": reps,
+            "timing": "eager launches" if eager else "hip graph replay"}
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -277,6 +284,8 @@ def main():
                     help="time only this precision's sweep (no headline line)")
     ap.add_argument("--sizes", type=str, default=None,
                     help="with --only: comma-separated sizes (N, or M for w4a16)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the sweep with eager launches instead of HIP graph replay")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 256 MiB device copy (reference dispatch for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -315,7 +324,7 @@ def main():
             for s in sizes:
                 M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else (s, s, s)
                 seed = inputs.config_seed(CONFIG_INDEX[prec], s)
-                e = sweep_entry(prec, M, N, K, seed, args.steps, args.warmup)
+                e = sweep_entry(prec, M, N, K, seed, args.steps, args.warmup, args.eager)
                 log(prec, e)
                 out[prec].append(e)
         print(json.dumps(out))
@@ -357,7 +366,7 @@ def main():
             for s in sizes:
                 M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else (s, s, s)
                 idx = CONFIG_INDEX["i8_512"] if (prec == "i8" and s == 512) else CONFIG_INDEX[prec]
-                e = sweep_entry(prec, M, N, K, inputs.config_seed(idx, s), 5, 2)
+                e = sweep_entry(prec, M, N, K, inputs.config_seed(idx, s), 5, 2, args.eager)
                 log(f"[bench] {prec} {M}x{N}x{K}: {e['us']} us, {e['throughput']} {e['unit']}, "
                     f"{e['roofline_bound']} frac {e['roofline_frac']}")
                 per[prec].append(e)
