@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(W4A16Problem p, int lg)
 //
 // The 4 wavefronts are arranged WN (columns) x WK (K quarters); the WK
 // partial sums meet in LDS. When the grid still has too few workgroups, K is
-// also split over KS workgroups: each writes its fp32 slice of Y to the
+// also split over KS workgroups: each writes its fp32 partial tile to the
 // workspace and a second kernel adds the slices in slice order.
 
 __device__ __forceinline__ f16x8 dequant8_natural(uint32_t w, _Float16 scale) {
@@ -525,35 +525,59 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
                     acc[i][j] += red[(((o * WN + wn) * MB + i) * NB + j) * 64 + lane];
     }
 
-    // 5. store: Y directly, or this K slice's fp32 part of Y
+    // 5. store Y directly, or this K slice's fp32 partial tile in the
+    //    threads' own register order (every store instruction writes 1 KiB
+    //    of contiguous memory); w4a16_reduce_kernel maps it back to (m, n)
+    if (sk.ks == 1) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + 16 * i + 4 * g + r, n = n0w + 16 * j + (lane & 15);
+                    if (m < p.M && n < p.N)
+                        p.Y[(int64_t)m * p.ldy + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
+                }
+        return;
+    }
+    // only the wavefronts with wk == 0 get here; they are the first WN
+    float *mine = sk.partial + (int64_t)logical * (BM * BN);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 16 * i + 4 * g + r, n = n0w + 16 * j + (lane & 15);
-                if (m < p.M && n < p.N) {
-                    if (sk.ks == 1)
-                        p.Y[(int64_t)m * p.ldy + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
-                    else
-                        sk.partial[((int64_t)ks * p.M + m) * p.N + n] = acc[i][j][r];
-                }
-            }
+            for (int r = 0; r < 4; ++r)
+                mine[((i * NB + j) * 4 + r) * (64 * WN) + tid] = acc[i][j][r];
 }
 
-// Y = fp16(sum of the KS fp32 slices), slices added in slice order.
-__global__ __launch_bounds__(256) void w4a16_reduce_kernel(W4A16Problem p, const float *partial, int ks) {
+// Y = fp16(sum of the KS fp32 partial tiles), slices added in slice order.
+// Partial tile layout (as written by w4a16_slice_kernel): element
+// ((i * NB + j) * 4 + r) * (64 * WN) + t holds row 16 i + 4 ((t % 64) / 16) + r
+// and column (t / 64) * 16 NB + 16 j + t % 16 of the BM x BN tile.
+template <int MB, int NB, int WN>
+__global__ __launch_bounds__(256) void w4a16_reduce_kernel(W4A16Problem p, W4A16Split sk) {
+    constexpr int BM = 16 * MB, BN = 16 * NB * WN, TILE = BM * BN;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)p.M * p.N;
-    if (e >= total)
+    const int64_t tiles = (int64_t)sk.mblocks * sk.ngroups;
+    if (e >= tiles * TILE)
         return;
+    const int tile = (int)(e / TILE), q = (int)(e % TILE);
+    const int t = q % (64 * WN), reg = q / (64 * WN);
+    const int r = reg % 4, j = (reg / 4) % NB, i = reg / (4 * NB);
+    const int lane = t % 64, wn = t / 64;
+    const int mb = tile % sk.mblocks, ng = tile / sk.mblocks;
+    const int m = mb * BM + 16 * i + 4 * (lane / 16) + r;
+    const int n = ng * BN + wn * 16 * NB + 16 * j + lane % 16;
+    const float *src = sk.partial + (int64_t)tile * sk.ks * TILE + q;
     float y = 0.f;
-    for (int o = 0; o < ks; ++o)
-        y += partial[o * total + e];
-    const int64_t m = e / p.N, n = e - m * p.N;
-    p.Y[m * p.ldy + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
+    for (int o = 0; o < sk.ks; ++o)
+        y += src[(int64_t)o * TILE];
+    if (m < p.M && n < p.N)
+        p.Y[(int64_t)m * p.ldy + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
 }
+
 
 template <int MT, int WN, int WK, int U>
 static hipError_t launch_cfg(const W4A16Problem &p, hipStream_t stream, int lg) {
@@ -603,7 +627,7 @@ static hipError_t launch_slice(const W4A16Problem &p, const W4A16Workspace &ws, 
     const int steps = (p.K + 127) / 128;
     const int spk = (steps + ks - 1) / ks;
     ks = (steps + spk - 1) / spk;
-    if (ks > 1 && (int64_t)ks * p.M * p.N > ws.partial_floats)
+    if (ks > 1 && tiles * ks * BM * BN > ws.partial_floats)
         return hipErrorOutOfMemory;   // caller falls back to a configuration without a workspace
     sk.ks = ks;
     sk.kslice = 128 * spk;
@@ -615,9 +639,9 @@ static hipError_t launch_slice(const W4A16Problem &p, const W4A16Workspace &ws, 
                        p, sk, lg);
     if (ks == 1)
         return hipGetLastError();
-    const int64_t total = (int64_t)p.M * p.N;
-    hipLaunchKernelGGL(w4a16_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p,
-                       (const float *)ws.partial, ks);
+    const int64_t total = tiles * BM * BN;
+    hipLaunchKernelGGL((w4a16_reduce_kernel<MB, NB, WN>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                       stream, p, sk);
     return hipGetLastError();
 }
 
