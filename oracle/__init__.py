@@ -40,6 +40,8 @@ def lib():
         L.oracle_gemm_w4a16.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64,
                                         _p, _i64, _i64, _p, _i64, _p, _i64]
         L.oracle_gemm_w4a16.restype = ctypes.c_int
+        L.oracle_quantize_w4.argtypes = [_i64, _i64, _p, _i64, _i64, _p, _i64, _p, _i64]
+        L.oracle_quantize_w4.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
         _lib = L
@@ -149,3 +151,19 @@ def gemm_w4a16(X, Wp, S, K, G, want_t2=False):
     if st != OK:
         raise ValueError(f"oracle_gemm_w4a16 status {st}")
     return (Y, T2) if want_t2 else Y
+
+
+def quantize_w4(W, G):
+    """Symmetric per-(row, group) INT4 quantisation of fp16 weights W (N x K):
+    returns (packed Q as N x K/2 uint8, scales S as N x K/G float16)."""
+    W = np.asarray(W)
+    if W.dtype == np.float16:
+        W = W.view(np.uint16)
+    W, ldw = _rows(W, np.uint16)
+    N, K = W.shape
+    Q = np.zeros((N, (K + 1) // 2), dtype=np.uint8)
+    S = np.zeros((N, K // G if G > 0 else 0), dtype=np.uint16)
+    st = lib().oracle_quantize_w4(N, K, _ptr(W), ldw, G, _ptr(Q), 2 * Q.shape[1], _ptr(S), max(S.shape[1], 1))
+    if st != OK:
+        raise ValueError(f"oracle_quantize_w4 status {st}")
+    return Q, S.view(np.float16)

@@ -226,6 +226,48 @@ int oracle_gemm_w4a16(int64_t M, int64_t N, int64_t K,
     return ORACLE_OK;
 }
 
+int oracle_quantize_w4(int64_t N, int64_t K, const uint16_t *W, int64_t ldw, int64_t G,
+                       uint8_t *Q, int64_t ldq, uint16_t *S, int64_t lds)
+{
+    if (N < 0 || K < 0 || G < 1 || (K % G) != 0 || (K % 2) != 0 || (ldq % 2) != 0)
+        return ORACLE_ERR_ARG;
+    if (N == 0 || K == 0)
+        return ORACLE_OK;
+    if (!W || !Q || !S || ldw < K || ldq < K || lds < K / G)
+        return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < N; ++n) {
+        uint8_t *qrow = Q + n * (ldq / 2);
+        for (int64_t k = 0; k < K / 2; ++k)
+            qrow[k] = 0;
+        for (int64_t g = 0; g < K / G; ++g) {
+            /* step 1: the group's largest magnitude */
+            double amax = 0.0;
+            for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+                double a = fabs(oracle_f16_decode(W[n * ldw + k]));
+                if (a > amax)
+                    amax = a;
+            }
+            /* step 2: the scale, amax / 7 rounded to binary16 */
+            uint16_t sbits = oracle_f16_encode_rne(amax / 7.0);
+            double s = oracle_f16_decode(sbits);
+            S[n * lds + g] = sbits;
+            /* step 3: each weight divided by the stored scale, rounded to the
+               nearest integer (ties to even), clamped to the signed 4-bit range */
+            for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+                int q = 0;
+                if (s > 0.0) {
+                    double r = nearbyint(oracle_f16_decode(W[n * ldw + k]) / s);
+                    q = r > 7.0 ? 7 : (r < -8.0 ? -8 : (int)r);
+                }
+                const uint8_t nib = (uint8_t)(q & 0xF);
+                qrow[k / 2] |= (uint8_t)((k % 2) ? (nib << 4) : nib);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
 int oracle_threads(void)
 {
 #ifdef _OPENMP

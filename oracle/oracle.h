@@ -87,6 +87,18 @@ int oracle_gemm_w4a16(int64_t M, int64_t N, int64_t K,
                       const uint16_t *S, int64_t lds, int64_t G,
                       double *Y, int64_t ldy, double *T2, int64_t ldt);
 
+/* Symmetric round-to-nearest INT4 quantisation of fp16 weights per
+ * (row, G-wide K group), the step that produces the inputs of
+ * oracle_gemm_w4a16 ([SM75] feature list: per-group scales, group_size = 128,
+ * packed INT4 weights; the pages give no formula, the reading used is):
+ *   s = binary16_rne(max_k |w| / 7)
+ *   q = clamp(round_half_even(w / s), -8, 7), q = 0 when s == 0
+ * W: N x K binary16 (row stride ldw elements); Q: packed like the GEMM's
+ * weights (row stride ldq nibbles, even); S: N x K/G binary16 (row stride lds).
+ * Requires K % G == 0 and K even. Inputs must be finite. */
+int oracle_quantize_w4(int64_t N, int64_t K, const uint16_t *W, int64_t ldw, int64_t G,
+                       uint8_t *Q, int64_t ldq, uint16_t *S, int64_t lds);
+
 /* Number of OpenMP threads a call uses. */
 int oracle_threads(void);
 

@@ -358,3 +358,90 @@ def test_w4a16_bad_group_rejected(oracle_lib):
     X, Wp, S = _w4a16_case(25, 1, 2, 16, 4)
     with pytest.raises(ValueError):
         oracle_lib.gemm_w4a16(X, Wp, S, 16, 5)           # K % G != 0
+
+
+# ------------------------------------------------------------------ INT4 weight quantisation
+
+def test_quantize_golden_worked_example(oracle_lib):
+    """tests/golden/quantize_w4_1x8.txt: two groups worked out by hand."""
+    f = {}
+    for line in open(os.path.join(GOLDEN, "quantize_w4_1x8.txt")):
+        if line.strip() and not line.startswith("#"):
+            key, *vals = line.split()
+            f[key] = vals
+    G = int(f["G"][0])
+    W = np.array([[float(v) for v in f["w"]]], dtype=np.float16)
+    Q, S = oracle_lib.quantize_w4(W, G)
+    num = [int(v) for v in f["s_num"]]
+    assert S.astype(np.float64).tolist() == [[num[0] / num[1], num[2] / num[3]]]
+    assert Q.tolist() == [[int(v) for v in f["q_bytes"]]]
+
+
+def test_quantize_exact_multiples_round_trip_exactly(oracle_lib):
+    """Weights that are integer multiples of a power-of-two step whose group
+    maximum is 7 steps: the scale is the step itself and the codes are the
+    integers."""
+    rng = np.random.default_rng(3)
+    G, N = 32, 6
+    step = 2.0 ** -rng.integers(2, 10, N)
+    q = rng.integers(-7, 8, (N, 4 * G))
+    q[:, ::G] = 7                      # every group reaches +7 steps
+    W = (q * step[:, None]).astype(np.float16)
+    Q, S = oracle_lib.quantize_w4(W, G)
+    assert np.array_equal(S.astype(np.float64), np.repeat(step[:, None], 4, axis=1))
+    assert np.array_equal(unpack_i4(Q, 4 * G), q)
+
+
+def test_quantize_ties_round_to_even(oracle_lib):
+    """w / s exactly k + 1/2 rounds to the even integer; -8 is reachable only
+    through clamping, never through the symmetric scale."""
+    s = 2.0 ** -4
+    row = np.array([7, 2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5], dtype=np.float64) * s
+    W = np.tile(row, (1, 4)).astype(np.float16)     # G = 32: one group of 32
+    Q, S = oracle_lib.quantize_w4(W, 32)
+    assert float(S[0, 0]) == s
+    assert unpack_i4(Q, 32)[0, :8].tolist() == [7, 2, 4, -2, -4, 0, 0, 2]
+
+
+def test_quantize_zero_group_and_bound(oracle_lib):
+    """An all-zero group has scale 0 and codes 0; elsewhere every weight is
+    within half a step of its dequantised value, and the group maximum maps to
+    +-7."""
+    rng = np.random.default_rng(11)
+    N, K, G = 8, 256, 64
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    W[3, 64:128] = 0
+    Q, S = oracle_lib.quantize_w4(W, G)
+    q = unpack_i4(Q, K)
+    s = np.repeat(S.astype(np.float64), G, axis=1)
+    assert S[3, 1] == 0 and np.all(q[3, 64:128] == 0)
+    w = W.astype(np.float64)
+    live = s > 0
+    assert np.all(np.abs(w - q * s)[live] <= s[live] / 2)
+    assert np.all(np.abs(q) <= 7)
+    for n in range(N):
+        for g in range(K // G):
+            grp = w[n, g * G:(g + 1) * G]
+            if np.any(grp != 0):
+                i = np.argmax(np.abs(grp))
+                assert abs(q[n, g * G + i]) == 7
+
+
+def test_quantize_then_w4a16_one_hot_returns_dequantised_weight(oracle_lib):
+    """Quantiser and weight-only GEMM share the packed layout: x = e_k gives
+    y[n] = q(n, k) * s(n, k / G)."""
+    rng = np.random.default_rng(5)
+    N, K, G = 12, 128, 32
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float16)
+    Q, S = oracle_lib.quantize_w4(W, G)
+    q = unpack_i4(Q, K)
+    for k in (0, 1, 31, 32, 127):
+        X = np.zeros((1, K), dtype=np.float16)
+        X[0, k] = 1
+        y = oracle_lib.gemm_w4a16(X, Q, S, K, G)
+        assert np.array_equal(y[0], q[:, k] * S[:, k // G].astype(np.float64))
+
+
+def test_quantize_bad_arguments(oracle_lib):
+    with pytest.raises(ValueError):
+        oracle_lib.quantize_w4(np.zeros((2, 96), np.float16), 64)    # K % G != 0
