@@ -6,8 +6,9 @@ One step is one FP16 GEMM C = A * B^T at M = N = K = 8192 (the FP16 square
 workload at its largest size) with inputs resident in HBM; `value` is its
 throughput. The same run also measures every precision at every size of the
 workloads (FP16/INT8/INT4 square N = 512 ... 8192, W4A16 4096 x 4096 at
-M = 1, 16, 128) and one pass of the whole hot path (all of those ops at their
-largest size), reported under `per_precision` and `hot_path`.
+M = 1, 16, 128), the INT4 weight quantiser at N = K = 4096 and 8192 (G = 128),
+and one pass of the whole GEMM hot path (all of those GEMMs at their largest
+size), reported under `per_precision` and `hot_path`.
 
 Timing: HIP events recorded on the stream the kernels are launched on (torch's
 current stream), W warm-up launches, then K timed launches between two
@@ -15,7 +16,7 @@ synchronisations. Small problems rotate through enough distinct input copies
 that the 256 MB Infinity Cache cannot serve repeats ("cold").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
-                       [--no-cpu-baseline] [--only f16|i8|i4|w4a16]
+                       [--no-cpu-baseline] [--only f16|i8|i4|w4a16|quantize] [--eager]
 """
 import argparse
 import hashlib
@@ -41,7 +42,8 @@ SQUARE_SIZES = [512, 1024, 2048, 4096, 8192]
 W4A16_M = [1, 16, 128]
 W4A16_NK = 4096
 W4A16_G = 128
-CONFIG_INDEX = {"i8_512": 0, "f16": 1, "i8": 2, "i4": 3, "w4a16": 4}
+CONFIG_INDEX = {"i8_512": 0, "f16": 1, "i8": 2, "i4": 3, "w4a16": 4, "quantize": 5}
+QUANT_NK = [4096, 8192]   # N = K of the weight matrices quantised (G = 128)
 
 
 def log(*a):
@@ -82,13 +84,15 @@ def algorithmic_bytes(prec, M, N, K, G=W4A16_G):
         return (M * K + N * K) // 2 + 4 * M * N
     if prec == "w4a16":
         return 2 * M * K + N * K // 2 + 2 * N * (K // G) + 2 * M * N
+    if prec == "quantize":   # read fp16 W, write packed codes and scales
+        return 2 * N * K + N * K // 2 + 2 * N * (K // G)
     raise ValueError(prec)
 
 
 def roofline(prec, M, N, K, seconds):
-    ops = 2.0 * M * N * K
+    ops = 2.0 * M * N * K if prec != "quantize" else 0.0
     nbytes = algorithmic_bytes(prec, M, N, K)
-    if prec == "w4a16":
+    if prec in ("w4a16", "quantize"):
         peak_ops = PEAK["f16"] * 1e12
     else:
         peak_ops = PEAK[prec] * 1e12
@@ -117,7 +121,12 @@ class Problem:
         import torch
         from precision_dense_gemm_tiled_amd import inputs
         self.prec, self.M, self.N, self.K = prec, M, N, K
-        if prec == "w4a16":
+        if prec == "quantize":
+            W = torch.from_numpy(inputs.f16_weights(seed, 0, N, K)).cuda()
+            self.ins = [W] + [W.clone() for _ in range(copies - 1)]
+            self.out = (torch.empty((N, K // 2), dtype=torch.uint8, device="cuda"),
+                        torch.empty((N, K // W4A16_G), dtype=torch.float16, device="cuda"))
+        elif prec == "w4a16":
             X, W, S = inputs.w4a16_problem(M, N, K, W4A16_G, seed)
             x, w, s = (torch.from_numpy(v).cuda() for v in (X, W, S))
             # rotate weights+scales (the streamed operand); activations stay put
@@ -141,6 +150,8 @@ class Problem:
             mp.gemm_i8(ins[0], ins[1], out=self.out)
         elif self.prec == "i4":
             mp.gemm_i4(ins[0], ins[1], self.K, out=self.out)
+        elif self.prec == "quantize":
+            mp.quantize_w4(ins, W4A16_G, out_q=self.out[0], out_s=self.out[1])
         else:
             mp.gemm_w4a16(ins[0], ins[1], ins[2], W4A16_G, out=self.out)
 
@@ -188,11 +199,12 @@ def time_graph(prob, launches, replays):
             prob.launch()
     g.replay()
     torch.cuda.synchronize()
-    replayed = prob.out.clone()
+    outs = prob.out if isinstance(prob.out, tuple) else (prob.out,)
+    replayed = [o.clone() for o in outs]
     prob.i = launches - 1
     prob.launch()
     torch.cuda.synchronize()
-    if not torch.equal(replayed, prob.out):
+    if not all(torch.equal(r, o) for r, o in zip(replayed, outs)):
         raise RuntimeError("graph replay output differs from the eager launch")
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -226,8 +238,11 @@ def sweep_entry(prec, M, N, K, seed, steps, warmup, eager=False):
     import torch
     torch.cuda.empty_cache()
     unit = "TFLOP/s" if prec in ("f16", "w4a16") else "TOP/s"
+    thr = 2.0 * M * N * K / t / 1e12
+    if prec == "quantize":
+        unit, thr = "GB/s", algorithmic_bytes(prec, M, N, K) / t / 1e9
     return {"M": M, "N": N, "K": K, "us": round(t * 1e6, 3),
-            "throughput": round(2.0 * M * N * K / t / 1e12, 3), "unit": unit,
+            "throughput": round(thr, 3), "unit": unit,
             "roofline_bound": rf["bound"], "roofline_frac": rf["frac"],
             "hbm_GBps_algorithmic": round(algorithmic_bytes(prec, M, N, K) / t / 1e9, 1),
             "input_copies": copies, "launches": reps,
@@ -280,7 +295,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["f16", "i8", "i4", "w4a16"], default=None,
+    ap.add_argument("--only", choices=["f16", "i8", "i4", "w4a16", "quantize"], default=None,
                     help="time only this precision's sweep (no headline line)")
     ap.add_argument("--sizes", type=str, default=None,
                     help="with --only: comma-separated sizes (N, or M for w4a16)")
@@ -317,12 +332,12 @@ def main():
         precs = [args.only]
         out = {}
         for prec in precs:
-            sizes = W4A16_M if prec == "w4a16" else SQUARE_SIZES
+            sizes = W4A16_M if prec == "w4a16" else (QUANT_NK if prec == "quantize" else SQUARE_SIZES)
             if args.sizes:
                 sizes = [int(v) for v in args.sizes.split(",")]
             out[prec] = []
             for s in sizes:
-                M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else (s, s, s)
+                M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else ((1, s, s) if prec == "quantize" else (s, s, s))
                 seed = inputs.config_seed(CONFIG_INDEX[prec], s)
                 e = sweep_entry(prec, M, N, K, seed, args.steps, args.warmup, args.eager)
                 log(prec, e)
@@ -360,11 +375,11 @@ def main():
 
     if not args.no_sweep:
         per = {}
-        for prec in ["f16", "i8", "i4", "w4a16"]:
-            sizes = W4A16_M if prec == "w4a16" else SQUARE_SIZES
+        for prec in ["f16", "i8", "i4", "w4a16", "quantize"]:
+            sizes = W4A16_M if prec == "w4a16" else (QUANT_NK if prec == "quantize" else SQUARE_SIZES)
             per[prec] = []
             for s in sizes:
-                M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else (s, s, s)
+                M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else ((1, s, s) if prec == "quantize" else (s, s, s))
                 idx = CONFIG_INDEX["i8_512"] if (prec == "i8" and s == 512) else CONFIG_INDEX[prec]
                 e = sweep_entry(prec, M, N, K, inputs.config_seed(idx, s), 5, 2, args.eager)
                 log(f"[bench] {prec} {M}x{N}x{K}: {e['us']} us, {e['throughput']} {e['unit']}, "

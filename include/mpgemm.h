@@ -136,6 +136,26 @@ mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_
                                  const uint16_t *S, int64_t lds, int64_t group_size,
                                  uint16_t *Y, int64_t ldy, void *stream);
 
+/* Weight quantisation for mpgemm_run_w4a16 (the weights and scales it
+ * consumes: "fused-int4-gemm-sm75" README, feature list: per-group scaling
+ * factors, group_size = 128, packed INT4 weights; the README names no
+ * formula, so the plainest symmetric round-to-nearest reading):
+ *   S[n][g] = fp16_rne(max |W[n][k]| over k in group g, divided by 7)
+ *   q(n, k) = clamp(round_half_even(W[n][k] / S[n][k / G]), -8, 7),
+ *             q = 0 where the scale is 0
+ * W:  N x K binary16 weights, row stride ldw elements; finite values.
+ * Wq: N x K signed INT4 written packed exactly as mpgemm_run_w4a16 reads
+ *     them, row stride ldwq nibbles (even); S: N x (K / G) binary16, row
+ *     stride lds elements. G must be a power of two with 32 <= G <= 512 and
+ *     K % G == 0 (else MPGEMM_ERR_UNSUPPORTED). W must be 16-byte aligned with
+ *     a row stride that is a multiple of 16 bytes, Wq 4-byte aligned with a
+ *     row stride that is a multiple of 4 bytes, S 2-byte aligned.
+ * Results are bit-identical to the definition above in exact arithmetic. */
+mpgemm_status_t mpgemm_quantize_w4(mpgemm_handle_t h, int64_t N, int64_t K,
+                                   const uint16_t *W, int64_t ldw, int64_t group_size,
+                                   uint8_t *Wq, int64_t ldwq, uint16_t *S, int64_t lds,
+                                   void *stream);
+
 #ifdef __cplusplus
 }
 #endif

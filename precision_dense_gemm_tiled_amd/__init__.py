@@ -13,8 +13,8 @@ import os
 __all__ = [
     "MpgemmError", "lib", "lib_path",
     "mpgemm_create", "mpgemm_destroy", "mpgemm_status_string",
-    "mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16",
-    "Handle", "default_handle", "gemm_f16", "gemm_i8", "gemm_i4", "gemm_w4a16",
+    "mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_quantize_w4",
+    "Handle", "default_handle", "gemm_f16", "gemm_i8", "gemm_i4", "gemm_w4a16", "quantize_w4",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.mpgemm_run_w4a16.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
                                        _vp, _i64, _i64, _vp, _i64, _vp]
         L.mpgemm_run_w4a16.restype = ctypes.c_int
+        L.mpgemm_quantize_w4.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
+        L.mpgemm_quantize_w4.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -97,6 +99,10 @@ def mpgemm_run_i4(h, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
 
 def mpgemm_run_w4a16(h, M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, stream=None) -> int:
     return lib().mpgemm_run_w4a16(h, M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, stream)
+
+
+def mpgemm_quantize_w4(h, N, K, W, ldw, group_size, Wq, ldwq, S, lds, stream=None) -> int:
+    return lib().mpgemm_quantize_w4(h, N, K, W, ldw, group_size, Wq, ldwq, S, lds, stream)
 
 
 # ------------------------------------------------------------------ torch helpers
@@ -223,3 +229,21 @@ def gemm_w4a16(X, Wq, S, group_size, out=None, handle=None, stream=None):
                             S.data_ptr(), lds, group_size, Y.data_ptr(), ldy, _stream(stream)),
            "mpgemm_run_w4a16")
     return Y
+
+
+def quantize_w4(W, group_size, out_q=None, out_s=None, handle=None, stream=None):
+    """Symmetric per-(row, group) INT4 quantisation of fp16 weights W (N x K):
+    returns packed Wq (N x K/2 uint8) and fp16 scales S (N x K/G), the inputs
+    of gemm_w4a16."""
+    import torch
+    ldw = _rows(W, torch.float16, "W")
+    N, K = W.shape
+    Q = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device) if out_q is None else out_q
+    S = (torch.empty((N, K // group_size if group_size > 0 else 0), dtype=torch.float16, device=W.device)
+         if out_s is None else out_s)
+    ldq_b = _rows(Q, torch.uint8, "Wq")
+    lds = _rows(S, torch.float16, "S")
+    h = default_handle(W.device.index) if handle is None else handle
+    _check(mpgemm_quantize_w4(h, N, K, W.data_ptr(), ldw, group_size, Q.data_ptr(), 2 * ldq_b,
+                              S.data_ptr(), lds, _stream(stream)), "mpgemm_quantize_w4")
+    return Q, S

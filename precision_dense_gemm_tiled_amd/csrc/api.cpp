@@ -261,3 +261,41 @@ mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_
 }
 
 }  // extern "C"
+
+mpgemm_status_t mpgemm_quantize_w4(mpgemm_handle_t h, int64_t N, int64_t K, const uint16_t *W, int64_t ldw,
+                                   int64_t group_size, uint8_t *Wq, int64_t ldwq, uint16_t *S, int64_t lds,
+                                   void *stream) {
+    if (N < 0 || K < 0)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (N == 0 || K == 0)
+        return MPGEMM_OK;
+    if (!W || !Wq || !S)
+        return MPGEMM_ERR_INVALID_ARG;
+    const bool pow2 = group_size > 0 && (group_size & (group_size - 1)) == 0;
+    if (!pow2 || group_size < 32 || group_size > 512 || K % group_size != 0)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if (ldw < K || ldwq < K || lds < K / group_size)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (N > INT_MAX || K > INT_MAX || (ldwq % 2) != 0)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if (!aligned16(W) || (ldw * 2) % 16 != 0 || (reinterpret_cast<uintptr_t>(Wq) & 3u) != 0 ||
+        (ldwq / 2) % 4 != 0 || (reinterpret_cast<uintptr_t>(S) & 1u) != 0)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if (!h)
+        return MPGEMM_ERR_INVALID_ARG;
+    mpgemm_status_t st = bind_device(h);
+    if (st != MPGEMM_OK)
+        return st;
+    mpg::QuantizeW4Problem p;
+    p.W = W;
+    p.Q = Wq;
+    p.S = S;
+    p.ldw = ldw;
+    p.ldq_b = ldwq / 2;
+    p.lds = lds;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.G = (int)group_size;
+    hipError_t e = mpg::launch_quantize_w4(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
+}

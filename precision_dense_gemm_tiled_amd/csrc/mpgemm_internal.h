@@ -86,4 +86,15 @@ int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a16(const W4A16Problem &p, int cfg, const W4A16Workspace &ws, int cu_count,
                         hipStream_t stream);
 
+// Symmetric INT4 quantisation of fp16 weights per (row, G-wide K group).
+struct QuantizeW4Problem {
+    const uint16_t *W;   // N x K fp16
+    uint8_t *Q;          // N x K packed int4
+    uint16_t *S;         // N x K/G fp16 scales
+    int64_t ldw, ldq_b, lds;
+    int N, K, G;
+};
+
+hipError_t launch_quantize_w4(const QuantizeW4Problem &p, hipStream_t stream);
+
 }  // namespace mpg

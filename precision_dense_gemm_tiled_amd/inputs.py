@@ -18,6 +18,7 @@ fused-int4-gemm-sm75 README, with the distributions of their stated configs):
   fp16 U[lo, hi)   lo + (hi - lo) * u with u = (draw >> 11) * 2^-53,
                    rounded to binary16 by numpy (round to nearest even)
   fp16 N(0, 1)     Box-Muller on two draws, rounded to binary16
+  fp16 weights     0.02 * N(0, 1) the same way (inputs of the quantiser)
 """
 import math
 
@@ -103,6 +104,17 @@ def f16_normal(seed: int, start: int, rows: int, cols: int) -> np.ndarray:
     u1 = ((r[0::2] >> _S11).view(np.int64).astype(np.float64) + 1.0) * (2.0 ** -53)   # (0, 1]
     u2 = (r[1::2] >> _S11).view(np.int64).astype(np.float64) * (2.0 ** -53)           # [0, 1)
     z = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * math.pi * u2)
+    return z.astype(np.float16).reshape(rows, cols)
+
+
+def f16_weights(seed: int, start: int, rows: int, cols: int, std: float = 0.02) -> np.ndarray:
+    """fp16 weights std * N(0, 1): Box-Muller on two draws, scaled in double,
+    rounded to binary16 once."""
+    n = rows * cols
+    r = splitmix64(seed, start, 2 * n)
+    u1 = ((r[0::2] >> _S11).view(np.int64).astype(np.float64) + 1.0) * (2.0 ** -53)
+    u2 = (r[1::2] >> _S11).view(np.int64).astype(np.float64) * (2.0 ** -53)
+    z = std * np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * math.pi * u2)
     return z.astype(np.float16).reshape(rows, cols)
 
 

@@ -30,7 +30,7 @@ def declared_symbols():
 def test_header_declares_the_abi():
     names = declared_symbols()
     for n in ["mpgemm_create", "mpgemm_destroy", "mpgemm_status_string", "mpgemm_run_f16",
-              "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16"]:
+              "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_quantize_w4"]:
         assert n in names
 
 
@@ -116,3 +116,25 @@ def test_gemm_argument_errors_without_device(mp, call, expect):
 ])
 def test_w4a16_argument_errors_without_device(mp, args, expect):
     assert mp.mpgemm_run_w4a16(None, *args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((16, 256, A, 256, 128, B, 256, S, 2), 1),       # valid: NULL handle left
+    ((-1, 256, A, 256, 128, B, 256, S, 2), 1),      # negative size
+    ((0, 256, 0, 256, 128, 0, 256, 0, 2), 0),       # N = 0: no-op
+    ((16, 0, 0, 0, 128, 0, 0, 0, 0), 0),            # K = 0: no-op
+    ((16, 256, A, 256, 100, B, 256, S, 2), 2),      # G not a power of two
+    ((16, 256, A, 256, 16, B, 256, S, 16), 2),      # G below 32
+    ((16, 2048, A, 2048, 1024, B, 2048, S, 2), 2),  # G above 512
+    ((16, 192, A, 192, 128, B, 192, S, 2), 2),      # K % G != 0
+    ((16, 256, A, 200, 128, B, 256, S, 2), 1),      # ldw < K
+    ((16, 256, A, 256, 128, B, 256, S, 1), 1),      # lds < K / G
+    ((16, 256, A + 2, 256, 128, B, 256, S, 2), 2),  # W not 16-byte aligned
+    ((16, 256, A, 260, 128, B, 256, S, 2), 2),      # W row stride not 16 bytes
+    ((16, 256, A, 256, 128, B + 2, 256, S, 2), 2),  # Wq not 4-byte aligned
+    ((16, 256, A, 256, 128, B, 258, S, 2), 2),      # Wq row stride not 4 bytes
+    ((16, 256, A, 256, 128, B, 256, S + 1, 2), 2),  # S not 2-byte aligned
+    ((16, 256, 0, 256, 128, B, 256, S, 2), 1),      # NULL weights
+])
+def test_quantize_argument_errors_without_device(mp, args, expect):
+    assert mp.mpgemm_quantize_w4(None, *args, None) == expect

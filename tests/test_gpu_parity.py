@@ -333,6 +333,63 @@ def test_w4a16_strided():
     assert np.all(whole[:, N:] == -7.0)
 
 
+# ------------------------------------------------------------------ INT4 weight quantisation
+
+def _quant(W, G, h=None):
+    q, sc = mp.quantize_w4(dev(W), G, handle=h)
+    return host(q), host(sc).view(np.uint16)
+
+
+@pytest.mark.parametrize("N,K,G", [(4096, 4096, 128), (37, 96, 32), (5, 640, 64), (8, 1536, 256),
+                                   (3, 2048, 512), (1, 512, 512), (130, 4096, 32)])
+def test_quantize_bit_exact(N, K, G):
+    """Packed codes and fp16 scales identical to the oracle, bit for bit
+    (4096 x 4096, G = 128 is the weight-only GEMM's layer)."""
+    W = inputs.f16_weights(N * 7 + K + G, 0, N, K)
+    Q, S = _quant(W, G)
+    Qr, Sr = oracle.quantize_w4(W, G)
+    assert np.array_equal(Q, Qr)
+    assert np.array_equal(S, Sr.view(np.uint16))
+
+
+def test_quantize_edge_values():
+    """Zero groups, one nonzero weight, exact ties, subnormal and maximal
+    fp16 weights."""
+    G, K = 32, 256
+    W = np.zeros((6, K), dtype=np.float64)
+    W[1, 5] = -0.25                                    # single nonzero: q = -7
+    W[2, :8] = np.array([7, 2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5]) * 2.0 ** -4   # ties
+    W[3, 32:64] = 2.0 ** -24 * np.arange(32)           # subnormals
+    W[4, 64:96] = np.linspace(-65504, 65504, 32)       # extremes
+    W[5] = np.random.default_rng(2).standard_normal(K)
+    W = W.astype(np.float16)
+    Q, S = _quant(W, G)
+    Qr, Sr = oracle.quantize_w4(W, G)
+    assert np.array_equal(Q, Qr)
+    assert np.array_equal(S, Sr.view(np.uint16))
+    assert np.all(S[0] == 0) and np.all(Q[0] == 0)
+
+
+def test_quantize_strided_and_feeds_w4a16():
+    """Row strides beyond K on every operand, bytes outside untouched; the
+    quantised weights drive the weight-only GEMM to the oracle's result."""
+    import torch
+    N, K, G, M = 24, 512, 128, 3
+    W = inputs.f16_weights(99, 0, N, K)
+    Wb = np.full((N, K + 64), np.nan, np.float16); Wb[:, :K] = W
+    qbig = torch.full((N, K // 2 + 16), 0x5A, dtype=torch.uint8, device="cuda")
+    sbig = torch.full((N, K // G + 3), -3.0, dtype=torch.float16, device="cuda")
+    mp.quantize_w4(dev(Wb)[:, :K], G, out_q=qbig[:, :K // 2], out_s=sbig[:, :K // G])
+    Qr, Sr = oracle.quantize_w4(W, G)
+    qh, sh = host(qbig), host(sbig)
+    assert np.array_equal(qh[:, :K // 2], Qr) and np.all(qh[:, K // 2:] == 0x5A)
+    assert np.array_equal(sh[:, :K // G].view(np.uint16), Sr.view(np.uint16)) and np.all(sh[:, K // G:] == -3.0)
+    X = inputs.f16_normal(7, 0, M, K)
+    y = host(mp.gemm_w4a16(dev(X), qbig[:, :K // 2], sbig[:, :K // G], G)).astype(np.float64)
+    yr, t2 = oracle.gemm_w4a16(X, Qr, Sr, K, G, want_t2=True)
+    assert np.all(np.abs(y - yr) <= w4a16_tol(yr, t2, K))
+
+
 # ------------------------------------------------------------------ argument errors with a device
 
 def test_argument_errors_with_handle():
