@@ -40,6 +40,8 @@ def lib():
         L.oracle_gemm_w4a16.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64,
                                         _p, _i64, _i64, _p, _i64, _p, _i64]
         L.oracle_gemm_w4a16.restype = ctypes.c_int
+        L.oracle_gemm_w4a4.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _p, _i64]
+        L.oracle_gemm_w4a4.restype = ctypes.c_int
         L.oracle_quantize_w4.argtypes = [_i64, _i64, _p, _i64, _i64, _p, _i64, _p, _i64]
         L.oracle_quantize_w4.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
@@ -167,3 +169,21 @@ def quantize_w4(W, G):
     if st != OK:
         raise ValueError(f"oracle_quantize_w4 status {st}")
     return Q, S.view(np.float16)
+
+
+def gemm_w4a4(Ap, Bp, K, SX, SW, BIAS=None):
+    """Y = (sum_k qa qb) * SX[m] * SW[n] + BIAS[n] (double, unrounded)."""
+    def bits(v):
+        v = np.ascontiguousarray(np.asarray(v))
+        return v.view(np.uint16) if v.dtype == np.float16 else v.astype(np.uint16)
+    Ap, lda_b = _rows(Ap, np.uint8)
+    Bp, ldb_b = _rows(Bp, np.uint8)
+    M, N = Ap.shape[0], Bp.shape[0]
+    sx, sw = bits(SX), bits(SW)
+    b = bits(BIAS) if BIAS is not None else None
+    Y = np.zeros((M, N), dtype=np.float64)
+    st = lib().oracle_gemm_w4a4(M, N, K, _ptr(Ap), 2 * lda_b, _ptr(Bp), 2 * ldb_b,
+                                _ptr(sx), _ptr(sw), _ptr(b) if b is not None else None, _ptr(Y), N)
+    if st != OK:
+        raise ValueError(f"oracle_gemm_w4a4 status {st}")
+    return Y

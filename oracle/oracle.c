@@ -226,6 +226,36 @@ int oracle_gemm_w4a16(int64_t M, int64_t N, int64_t K,
     return ORACLE_OK;
 }
 
+int oracle_gemm_w4a4(int64_t M, int64_t N, int64_t K,
+                     const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                     const uint16_t *SX, const uint16_t *SW, const uint16_t *BIAS,
+                     double *Y, int64_t ldy)
+{
+    if ((K % 2) != 0 || (lda % 2) != 0 || (ldb % 2) != 0)
+        return ORACLE_ERR_ARG;
+    int st = check_dims(M, N, K, lda, ldb, ldy, A, B, Y);
+    if (st != ORACLE_OK || M == 0 || N == 0)
+        return st;
+    if (!SX || !SW)
+        return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint8_t *arow = A + m * (lda / 2);
+        const double sx = oracle_f16_decode(SX[m]);
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *brow = B + n * (ldb / 2);
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (int64_t)oracle_i4_get(arow, k) * (int64_t)oracle_i4_get(brow, k);
+            double y = (double)acc * sx * oracle_f16_decode(SW[n]);
+            if (BIAS)
+                y += oracle_f16_decode(BIAS[n]);
+            Y[m * ldy + n] = y;
+        }
+    }
+    return ORACLE_OK;
+}
+
 int oracle_quantize_w4(int64_t N, int64_t K, const uint16_t *W, int64_t ldw, int64_t G,
                        uint8_t *Q, int64_t ldq, uint16_t *S, int64_t lds)
 {

@@ -87,6 +87,18 @@ int oracle_gemm_w4a16(int64_t M, int64_t N, int64_t K,
                       const uint16_t *S, int64_t lds, int64_t G,
                       double *Y, int64_t ldy, double *T2, int64_t ldt);
 
+/* INT4 x INT4 GEMM with a scale epilogue ([W4A4] section 1: Y = (Q(X) Q(W)^T)
+ * (.) scale + b, both operands 4-bit). Reading of the scale: one fp16 factor
+ * per row of X (SX, M values) times one per row of W (SW, N values), applied to
+ * the exact integer product; BIAS (N values, may be NULL) added per column:
+ *   Y[m][n] = (sum_k qa(m,k) qb(n,k)) * SX[m] * SW[n] + BIAS[n]
+ * in double, unrounded (the tests round to fp16 where they compare). A, B
+ * packed as for oracle_gemm_i4. The low-rank branch L(X) is not part of it. */
+int oracle_gemm_w4a4(int64_t M, int64_t N, int64_t K,
+                     const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                     const uint16_t *SX, const uint16_t *SW, const uint16_t *BIAS,
+                     double *Y, int64_t ldy);
+
 /* Symmetric round-to-nearest INT4 quantisation of fp16 weights per
  * (row, G-wide K group), the step that produces the inputs of
  * oracle_gemm_w4a16 ([SM75] feature list: per-group scales, group_size = 128,

@@ -445,3 +445,51 @@ def test_quantize_then_w4a16_one_hot_returns_dequantised_weight(oracle_lib):
 def test_quantize_bad_arguments(oracle_lib):
     with pytest.raises(ValueError):
         oracle_lib.quantize_w4(np.zeros((2, 96), np.float16), 64)    # K % G != 0
+
+
+# ------------------------------------------------------------------ W4A4: INT4 x INT4 with scale epilogue
+
+def _pack(q):
+    q = np.asarray(q, dtype=np.int64) & 0xF
+    return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_w4a4_hand_worked_2x2(oracle_lib):
+    """qa = [[1, -2, 3, -8], [7, 0, -1, 2]], qb = [[2, 2, -1, 1], [-3, 4, 0, 5]]:
+    row0.col0 = 2 - 4 - 3 - 8 = -13; row0.col1 = -3 - 8 + 0 - 40 = -51;
+    row1.col0 = 14 + 0 + 1 + 2 = 17; row1.col1 = -21 + 0 + 0 + 10 = -11.
+    SX = [0.5, 2], SW = [0.25, -1], BIAS = [1, -0.5]:
+    Y = [[-13*0.125 + 1, -51*-0.5 - 0.5], [17*0.5 + 1, -11*-2 - 0.5]]
+      = [[-0.625, 25.0], [9.5, 21.5]]."""
+    qa = [[1, -2, 3, -8], [7, 0, -1, 2]]
+    qb = [[2, 2, -1, 1], [-3, 4, 0, 5]]
+    sx = np.array([0.5, 2], np.float16)
+    sw = np.array([0.25, -1], np.float16)
+    b = np.array([1, -0.5], np.float16)
+    y = oracle_lib.gemm_w4a4(_pack(qa), _pack(qb), 4, sx, sw, b)
+    assert y.tolist() == [[-0.625, 25.0], [9.5, 21.5]]
+
+
+def test_w4a4_unit_scales_equal_int4_gemm(oracle_lib):
+    """SX = SW = 1 and no bias: the exact INT4 product, element for element."""
+    from precision_dense_gemm_tiled_amd import inputs
+    M, N, K = 9, 13, 70
+    Ap, Bp = inputs.gemm_problem("i4", M, N, K, seed=12)
+    y = oracle_lib.gemm_w4a4(Ap, Bp, K, np.ones(M, np.float16), np.ones(N, np.float16))
+    assert np.array_equal(y, oracle_lib.gemm_i4(Ap, Bp, K).astype(np.float64))
+
+
+def test_w4a4_scales_and_bias_are_outer_product_and_column_shift(oracle_lib):
+    """Power-of-two scales multiply exactly: Y = C * sx[m] * sw[n] + b[n]
+    against the integer product C from the unit-scale call."""
+    from precision_dense_gemm_tiled_amd import inputs
+    M, N, K = 7, 11, 64
+    Ap, Bp = inputs.gemm_problem("i4", M, N, K, seed=21)
+    rng = np.random.default_rng(4)
+    sx = (2.0 ** rng.integers(-6, 3, M)).astype(np.float16)
+    sw = (-(2.0 ** rng.integers(-6, 3, N))).astype(np.float16)
+    b = rng.integers(-8, 8, N).astype(np.float16)
+    c = oracle_lib.gemm_w4a4(Ap, Bp, K, np.ones(M, np.float16), np.ones(N, np.float16))
+    y = oracle_lib.gemm_w4a4(Ap, Bp, K, sx, sw, b)
+    want = c * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] + b.astype(np.float64)[None, :]
+    assert np.array_equal(y, want)
