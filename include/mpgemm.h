@@ -10,6 +10,8 @@
  *                     int32 accumulate, int32 C (exact)
  *   mpgemm_run_w4a16  fp16 activations x int4 weights with per-(row, K-group)
  *                     fp16 scales, fp32 accumulate, fp16 Y
+ *   mpgemm_run_w4a4   int4 x int4 with per-row and per-column fp16 scales and
+ *                     a column bias applied to the exact int32 sum, fp16 Y
  *
  * Sources: "Hand-Written PTX Tensor-Core GEMM Kernels: A Multi-Precision Study
  * on NVIDIA L4" (abstract and summary: the FP16 / INT8 / INT4 GEMM problem over
@@ -114,6 +116,24 @@ mpgemm_status_t mpgemm_run_i4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K
                               const uint8_t *A, int64_t lda,
                               const uint8_t *B, int64_t ldb,
                               int32_t *C, int64_t ldc, void *stream);
+
+/* INT4 x INT4 GEMM with a scale epilogue ("Warp-Specialized Kernel
+ * Implementation for W4A4 MatMul on Latest GPU Architectures", section 1:
+ * Y = (Q(X) Q(W)^T) (.) scale + b with 4-bit activations and weights; the
+ * page gives no scale layout, the reading used is one factor per activation
+ * row and one per weight row, applied to the exact integer product, and a
+ * bias per output column; the low-rank branch L(X) is not part of it):
+ *   Y[m][n] = fp16( (sum_k qa(m, k) qb(n, k)) * SX[m] * SW[n] + bias[n] )
+ * A, B: packed signed INT4 exactly as for mpgemm_run_i4 (K, lda, ldb even,
+ * K <= MPGEMM_MAX_K_INT). SX: M binary16, SW: N binary16, bias: N binary16 or
+ * NULL (no bias); all 2-byte aligned. Y: M x N binary16, row stride ldy.
+ * The integer sum is exact; the two products and the bias are applied in
+ * fp32 (each correctly rounded), then one rounding to fp16 (nearest even). */
+mpgemm_status_t mpgemm_run_w4a4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                const uint8_t *A, int64_t lda,
+                                const uint8_t *B, int64_t ldb,
+                                const uint16_t *SX, const uint16_t *SW, const uint16_t *bias,
+                                uint16_t *Y, int64_t ldy, void *stream);
 
 /* Weight-only INT4 GEMM ("fused-int4-gemm-sm75" README: register
  * dequantisation, per-group scales with group_size = 128; decode M = 1 and

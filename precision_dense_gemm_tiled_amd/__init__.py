@@ -13,8 +13,8 @@ import os
 __all__ = [
     "MpgemmError", "lib", "lib_path",
     "mpgemm_create", "mpgemm_destroy", "mpgemm_status_string",
-    "mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_quantize_w4",
-    "Handle", "default_handle", "gemm_f16", "gemm_i8", "gemm_i4", "gemm_w4a16", "quantize_w4",
+    "mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_run_w4a4", "mpgemm_quantize_w4",
+    "Handle", "default_handle", "gemm_f16", "gemm_i8", "gemm_i4", "gemm_w4a16", "gemm_w4a4", "quantize_w4",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L.mpgemm_run_w4a16.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
                                        _vp, _i64, _i64, _vp, _i64, _vp]
         L.mpgemm_run_w4a16.restype = ctypes.c_int
+        L.mpgemm_run_w4a4.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
+                                      _vp, _i64, _vp]
+        L.mpgemm_run_w4a4.restype = ctypes.c_int
         L.mpgemm_quantize_w4.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
         L.mpgemm_quantize_w4.restype = ctypes.c_int
         _lib = L
@@ -99,6 +102,10 @@ def mpgemm_run_i4(h, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
 
 def mpgemm_run_w4a16(h, M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, stream=None) -> int:
     return lib().mpgemm_run_w4a16(h, M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, stream)
+
+
+def mpgemm_run_w4a4(h, M, N, K, A, lda, B, ldb, SX, SW, bias, Y, ldy, stream=None) -> int:
+    return lib().mpgemm_run_w4a4(h, M, N, K, A, lda, B, ldb, SX, SW, bias, Y, ldy, stream)
 
 
 def mpgemm_quantize_w4(h, N, K, W, ldw, group_size, Wq, ldwq, S, lds, stream=None) -> int:
@@ -247,3 +254,23 @@ def quantize_w4(W, group_size, out_q=None, out_s=None, handle=None, stream=None)
     _check(mpgemm_quantize_w4(h, N, K, W.data_ptr(), ldw, group_size, Q.data_ptr(), 2 * ldq_b,
                               S.data_ptr(), lds, _stream(stream)), "mpgemm_quantize_w4")
     return Q, S
+
+
+def gemm_w4a4(A, B, K, sx, sw, bias=None, out=None, handle=None, stream=None):
+    """Y = fp16((A_int4 @ B_int4.T) * sx[:, None] * sw[None, :] + bias): packed
+    INT4 A (M x K/2 uint8) and B (N x K/2 uint8), fp16 sx (M), sw (N), bias (N
+    or None) -> fp16 Y (M x N)."""
+    import torch
+    lda_b = _rows(A, torch.uint8, "A")
+    ldb_b = _rows(B, torch.uint8, "B")
+    M, N = A.shape[0], B.shape[0]
+    for name, v, n in (("sx", sx, M), ("sw", sw, N)) + ((("bias", bias, N),) if bias is not None else ()):
+        if v.dtype != torch.float16 or v.numel() != n or not v.is_contiguous() or not v.is_cuda:
+            raise ValueError(f"{name}: expected {n} contiguous fp16 values on the device")
+    Y = torch.empty((M, N), dtype=torch.float16, device=A.device) if out is None else out
+    ldy = _rows(Y, torch.float16, "Y")
+    h = default_handle(A.device.index) if handle is None else handle
+    _check(mpgemm_run_w4a4(h, M, N, K, A.data_ptr(), 2 * lda_b, B.data_ptr(), 2 * ldb_b, sx.data_ptr(),
+                           sw.data_ptr(), bias.data_ptr() if bias is not None else None, Y.data_ptr(), ldy,
+                           _stream(stream)), "mpgemm_run_w4a4")
+    return Y

@@ -26,9 +26,10 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Common checks of a C = A * B^T call. elem_num/elem_den: bytes per element
 // of A and B (1/2 for packed INT4); out_bytes: bytes per element of C.
-mpgemm_status_t check_gemm(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K, const void *A,
-                           int64_t lda, const void *B, int64_t ldb, const void *C, int64_t ldc,
-                           int elem_num, int elem_den, int out_bytes, int64_t max_k, bool *noop) {
+// Every argument check of a GEMM call except the handle.
+mpgemm_status_t check_gemm_args(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                                const void *B, int64_t ldb, const void *C, int64_t ldc, int elem_num,
+                                int elem_den, int out_bytes, int64_t max_k, bool *noop) {
     *noop = false;
     if (M < 0 || N < 0 || K < 0)
         return MPGEMM_ERR_INVALID_ARG;
@@ -52,11 +53,19 @@ mpgemm_status_t check_gemm(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K, c
     // byte-gather kernel).
     if ((reinterpret_cast<uintptr_t>(C) % out_bytes) != 0)
         return MPGEMM_ERR_UNSUPPORTED;
-    // the handle is checked last so that every argument error above is
-    // reported without a device (and can be tested on a host without a GPU)
-    if (!h)
-        return MPGEMM_ERR_INVALID_ARG;
     return MPGEMM_OK;
+}
+
+// The handle is checked last so that every argument error is reported without
+// a device (and can be tested on a host without a GPU).
+mpgemm_status_t check_gemm(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K, const void *A,
+                           int64_t lda, const void *B, int64_t ldb, const void *C, int64_t ldc,
+                           int elem_num, int elem_den, int out_bytes, int64_t max_k, bool *noop) {
+    mpgemm_status_t st =
+        check_gemm_args(M, N, K, A, lda, B, ldb, C, ldc, elem_num, elem_den, out_bytes, max_k, noop);
+    if (st != MPGEMM_OK || *noop)
+        return st;
+    return h ? MPGEMM_OK : MPGEMM_ERR_INVALID_ARG;
 }
 
 // Split-K workspace per handle: 32 MiB of fp32 partial sums.
@@ -73,7 +82,8 @@ mpgemm_status_t bind_device(mpgemm_handle_t h) {
 
 mpgemm_status_t run_tile(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int64_t kbytes,
                          const void *A, int64_t lda_b, const void *B, int64_t ldb_b, void *C,
-                         int64_t ldc, void *stream) {
+                         int64_t ldc, void *stream, const uint16_t *sx = nullptr,
+                         const uint16_t *sw = nullptr, const uint16_t *bias = nullptr) {
     mpgemm_status_t st = bind_device(h);
     if (st != MPGEMM_OK)
         return st;
@@ -87,6 +97,9 @@ mpgemm_status_t run_tile(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int6
     p.M = (int)M;
     p.N = (int)N;
     p.kbytes = kbytes;
+    p.sx = sx;
+    p.sw = sw;
+    p.bias = bias;
     int cfg = h->forced_tile_cfg >= 0 ? h->forced_tile_cfg
                                       : mpg::choose_tile_cfg(prec, M, N, kbytes, h->cu_count);
     hipError_t e = mpg::launch_gemm(prec, cfg, p, static_cast<hipStream_t>(stream));
@@ -207,6 +220,27 @@ mpgemm_status_t mpgemm_run_i4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K
     if (st != MPGEMM_OK || noop)
         return st;
     return run_tile(h, mpg::PREC_I4, M, N, K / 2, A, lda / 2, B, ldb / 2, C, ldc, stream);
+}
+
+mpgemm_status_t mpgemm_run_w4a4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                                const uint16_t *SX, const uint16_t *SW, const uint16_t *bias,
+                                uint16_t *Y, int64_t ldy, void *stream) {
+    if (M > 0 && N > 0 && K >= 0 && ((K % 2) != 0 || (lda % 2) != 0 || (ldb % 2) != 0))
+        return MPGEMM_ERR_UNSUPPORTED;
+    bool noop;
+    mpgemm_status_t st =
+        check_gemm_args(M, N, K, A, lda, B, ldb, Y, ldy, 1, 2, 2, MPGEMM_MAX_K_INT, &noop);
+    if (st != MPGEMM_OK || noop)
+        return st;
+    if (!SX || !SW)
+        return MPGEMM_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(SX) | reinterpret_cast<uintptr_t>(SW) |
+         reinterpret_cast<uintptr_t>(bias)) & 1u)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if (!h)
+        return MPGEMM_ERR_INVALID_ARG;
+    return run_tile(h, mpg::PREC_W4A4, M, N, K / 2, A, lda / 2, B, ldb / 2, Y, ldy, stream, SX, SW, bias);
 }
 
 mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,

@@ -33,6 +33,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 template <int P> struct AccOf { typedef i32x16 type; typedef int32_t out; };
 template <> struct AccOf<PREC_F16> { typedef f32x16 type; typedef float out; };
+template <> struct AccOf<PREC_W4A4> { typedef i32x16 type; typedef uint16_t out; };
 
 // XOR swizzle of the 16-byte chunk position within an LDS row. Fragment reads
 // take one chunk column across 8 (or 16) consecutive rows; the swizzle spreads
@@ -158,25 +159,53 @@ __device__ __forceinline__ void read_frags(const uint8_t *As, int step, int wm0,
 // row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the 32x32 block.
 template <int P, int TM, int TN>
 __device__ __forceinline__ void store_tile(const GemmProblem &p, int row0, int col0, int lane,
-                                           const typename AccOf<P>::type (&acc)[TM][TN]) {
+                                           const typename AccOf<P>::type (&acc)[TM][TN],
+                                           const float *fx = nullptr, const float *fw = nullptr,
+                                           const float *fb = nullptr) {
     typedef typename AccOf<P>::out out_t;
     out_t *C = reinterpret_cast<out_t *>(p.C);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = col0 + j * 32 + (lane & 31);
+            const int cl = j * 32 + (lane & 31);   // column within this wavefront's sub-tile
+            const int col = col0 + cl;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = row0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int rl = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int row = row0 + rl;
                 if (row < p.M && col < p.N) {
-                    if constexpr (P == PREC_I4)
+                    if constexpr (P == PREC_W4A4) {
+                        // |acc >> 8| <= 64 K < 2^24: exact in fp32; then two
+                        // products and the bias in fp32, one rounding to fp16
+                        const float y = (float)(acc[i][j][r] >> 8) * fx[rl] * fw[cl] + fb[cl];
+                        C[(int64_t)row * p.ldc + col] = __builtin_bit_cast(uint16_t, (_Float16)y);
+                    } else if constexpr (P == PREC_I4) {
                         C[(int64_t)row * p.ldc + col] = acc[i][j][r] >> 8;
-                    else
+                    } else {
                         C[(int64_t)row * p.ldc + col] = acc[i][j][r];
+                    }
                 }
             }
         }
+}
+
+// W4A4 epilogue factors of a BM x BN tile staged in LDS as fp32 (the operand
+// buffers are free once every wavefront is past its last fragment read):
+// fac[0, BM) = SX of the tile's rows, fac[BM, BM + BN) = SW of its columns,
+// fac[BM + BN, BM + 2 BN) = bias (0 without one). Entries past M or N are 0.
+template <int BM, int BN, int NT>
+__device__ __forceinline__ void stage_factors(const GemmProblem &p, int row0, int col0, int tid,
+                                              float *fac) {
+    __syncthreads();
+    for (int t = tid; t < BM; t += NT)
+        fac[t] = row0 + t < p.M ? (float)__builtin_bit_cast(_Float16, p.sx[row0 + t]) : 0.f;
+    for (int t = tid; t < BN; t += NT) {
+        const bool ok = col0 + t < p.N;
+        fac[BM + t] = ok ? (float)__builtin_bit_cast(_Float16, p.sw[col0 + t]) : 0.f;
+        fac[BM + BN + t] = ok && p.bias ? (float)__builtin_bit_cast(_Float16, p.bias[col0 + t]) : 0.f;
+    }
+    __syncthreads();
 }
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).
@@ -348,7 +377,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p
     }
     // the last entries' dummy loads must land before the wavefront exits
     wait_vm_lds<0>();
-    store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc);
+    if constexpr (P == PREC_W4A4) {
+        static_assert((BM + 2 * BN) * 4 <= NS * STAGE, "factor staging fits the ring");
+        float *fac = reinterpret_cast<float *>(smem);
+        stage_factors<BM, BN, NT>(p, row0, col0, tid, fac);
+        store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc, fac + wm0, fac + BM + wn0,
+                              fac + BM + BN + wn0);
+    } else {
+        store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc);
+    }
 }
 
 // Operands without 16-byte row alignment (or with rows too long for 32-bit
@@ -427,7 +464,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_generic_kernel(GemmP
             store(cur ^ 1, R);
         __syncthreads();
     }
-    store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc);
+    if constexpr (P == PREC_W4A4) {
+        static_assert((BM + 2 * BN) * 4 <= 2 * STAGE, "factor staging fits the buffers");
+        float *fac = reinterpret_cast<float *>(smem);
+        stage_factors<BM, BN, NT>(p, row0, col0, tid, fac);
+        store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc, fac + wm0, fac + BM + wn0,
+                              fac + BM + BN + wn0);
+    } else {
+        store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc);
+    }
 }
 
 // ------------------------------------------------------------------ launch
@@ -525,6 +570,7 @@ hipError_t launch_gemm(int prec, int cfg, const GemmProblem &p, hipStream_t stre
     case PREC_F16: return launch_prec<PREC_F16>(cfg, p, aligned, stream);
     case PREC_I8: return launch_prec<PREC_I8>(cfg, p, aligned, stream);
     case PREC_I4: return launch_prec<PREC_I4>(cfg, p, aligned, stream);
+    case PREC_W4A4: return launch_prec<PREC_W4A4>(cfg, p, aligned, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -7,7 +7,8 @@
 
 namespace mpg {
 
-enum Prec { PREC_F16 = 0, PREC_I8 = 1, PREC_I4 = 2 };
+// PREC_W4A4: the INT4 main loop with a scale epilogue (fp16 output).
+enum Prec { PREC_F16 = 0, PREC_I8 = 1, PREC_I4 = 2, PREC_W4A4 = 3 };
 
 // One dense GEMM C = A * B^T, described in bytes of the packed K dimension:
 // kbytes = 2K (f16), K (i8) or K/2 (i4). Row strides are in bytes for A and B
@@ -19,6 +20,9 @@ struct GemmProblem {
     int64_t lda_b, ldb_b, ldc;
     int M, N;
     int64_t kbytes;
+    // PREC_W4A4 epilogue: C[m][n] = fp16(acc * sx[m] * sw[n] + bias[n]) (fp16
+    // bits; bias may be null); unused by the other precisions
+    const uint16_t *sx, *sw, *bias;
 };
 
 // Tile configurations of the square/rectangular tile kernel. The index is

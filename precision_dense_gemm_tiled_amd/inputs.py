@@ -159,3 +159,17 @@ def w4a16_problem(M: int, N: int, K: int, G: int, seed: int):
     off += N * ((K + 1) // 2)
     S = f16_uniform(seed, off, N, K // G, 0.005, 0.02)
     return X, W, S
+
+
+def w4a4_problem(M: int, N: int, K: int, seed: int):
+    """Packed INT4 activations A (M x K/2) and weights B (N x K/2), uniform
+    [-8, 7]; fp16 per-row activation scales SX U[0.005, 0.02), per-row weight
+    scales SW U[0.001, 0.01), column bias 0.1 * N(0, 1)."""
+    nb = (K + 1) // 2
+    A = int4_packed_uniform(seed, 0, M, K)
+    B = int4_packed_uniform(seed, M * nb, N, K)
+    off = (M + N) * nb
+    SX = f16_uniform(seed, off, 1, M, 0.005, 0.02).reshape(M)
+    SW = f16_uniform(seed, off + M, 1, N, 0.001, 0.01).reshape(N)
+    bias = f16_weights(seed, off + M + N, 1, N, 0.1).reshape(N)
+    return A, B, SX, SW, bias

@@ -30,7 +30,7 @@ def declared_symbols():
 def test_header_declares_the_abi():
     names = declared_symbols()
     for n in ["mpgemm_create", "mpgemm_destroy", "mpgemm_status_string", "mpgemm_run_f16",
-              "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_quantize_w4"]:
+              "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_run_w4a4", "mpgemm_quantize_w4"]:
         assert n in names
 
 
@@ -138,3 +138,21 @@ def test_w4a16_argument_errors_without_device(mp, args, expect):
 ])
 def test_quantize_argument_errors_without_device(mp, args, expect):
     assert mp.mpgemm_quantize_w4(None, *args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((4, 4, 32, A, 32, B, 32, S, S + 64, S + 128, C, 16), 1),      # valid: NULL handle left
+    ((4, 4, 32, A, 32, B, 32, S, S + 64, 0, C, 16), 1),            # no bias is fine
+    ((0, 4, 32, 0, 32, 0, 32, 0, 0, 0, 0, 16), 0),                 # M = 0: no-op
+    ((4, 4, 31, A, 32, B, 32, S, S + 64, 0, C, 16), 2),            # odd K
+    ((4, 4, 32, A, 33, B, 32, S, S + 64, 0, C, 16), 2),            # odd lda
+    ((4, 4, 32, A, 32, B, 32, 0, S + 64, 0, C, 16), 1),            # no SX
+    ((4, 4, 32, A, 32, B, 32, S, 0, 0, C, 16), 1),                 # no SW
+    ((4, 4, 32, A, 32, B, 32, S + 1, S + 64, 0, C, 16), 2),        # SX not 2-byte aligned
+    ((4, 4, 32, A, 32, B, 32, S, S + 64, S + 129, C, 16), 2),      # bias not 2-byte aligned
+    ((4, 4, 32, A, 32, B, 32, S, S + 64, 0, C + 1, 16), 2),        # Y not 2-byte aligned
+    ((4, 8, 32, A, 32, B, 32, S, S + 64, 0, C, 4), 1),             # ldy < N
+    ((4, 4, 131072, A, 131072, B, 131072, S, S + 64, 0, C, 16), 2),  # K bound
+])
+def test_w4a4_argument_errors_without_device(mp, args, expect):
+    assert mp.mpgemm_run_w4a4(None, *args, None) == expect

@@ -333,6 +333,81 @@ def test_w4a16_strided():
     assert np.all(whole[:, N:] == -7.0)
 
 
+# ------------------------------------------------------------------ W4A4: INT4 x INT4 with scale epilogue
+
+def w4a4_tol(y, c_abs, sx, sw, b):
+    """fp16 output rounding (half an ulp: 2^-11 relative) plus the fp32 epilogue
+    (two products and one sum, each within 2^-24 relative) plus subnormals."""
+    mag = c_abs * np.abs(sx.astype(np.float64))[:, None] * np.abs(sw.astype(np.float64))[None, :]
+    bb = np.abs(b.astype(np.float64))[None, :] if b is not None else 0.0
+    return 2.0 ** -11 * np.abs(y) + 3 * 2.0 ** -24 * (mag + bb) + 2.0 ** -24
+
+
+def _w4a4_check(A, B, K, sx, sw, b, got, what):
+    y = oracle.gemm_w4a4(A, B, K, sx, sw, b)
+    c_abs = np.abs(oracle.gemm_i4(A, B, K).astype(np.float64))
+    err = np.abs(got.astype(np.float64) - y)
+    bad = np.argwhere(err > w4a4_tol(y, c_abs, sx, sw, b))
+    assert bad.size == 0, f"{what}: {len(bad)} outside the bar, worst {err.max()}"
+
+
+@pytest.mark.parametrize("M,N,K,with_bias", [(1, 1, 2, True), (64, 64, 128, True), (300, 520, 200, False),
+                                             (257, 129, 4096, True), (1024, 1024, 1024, True)])
+def test_w4a4_against_oracle(M, N, K, with_bias):
+    A, B, sx, sw, b = inputs.w4a4_problem(M, N, K, seed=M + 3 * N + K)
+    b = b if with_bias else None
+    got = host(mp.gemm_w4a4(dev(A), dev(B), K, dev(sx), dev(sw), dev(b) if b is not None else None))
+    _w4a4_check(A, B, K, sx, sw, b, got, f"w4a4 {M}x{N}x{K}")
+
+
+def test_w4a4_every_tile_config(monkeypatch):
+    M, N, K = 300, 520, 200
+    A, B, sx, sw, b = inputs.w4a4_problem(M, N, K, seed=78)
+    for cfg in range(12):
+        monkeypatch.setenv("MPGEMM_TILE_CFG", str(cfg))
+        with mp.Handle() as h:
+            got = host(mp.gemm_w4a4(dev(A), dev(B), K, dev(sx), dev(sw), dev(b), handle=h.value))
+        _w4a4_check(A, B, K, sx, sw, b, got, f"w4a4 cfg {cfg}")
+
+
+def test_w4a4_exact_when_representable():
+    """Power-of-two scales and integer bias: every output is exactly
+    representable in fp16 (|y| < 2048), so Y must match bit for bit."""
+    M, N, K = 96, 80, 64
+    A, B, _, _, _ = inputs.w4a4_problem(M, N, K, seed=5)
+    r = np.random.default_rng(6)
+    sx = (2.0 ** -r.integers(0, 4, M)).astype(np.float16)
+    sw = (2.0 ** -r.integers(0, 4, N)).astype(np.float16)
+    b = r.integers(-16, 16, N).astype(np.float16)
+    got = host(mp.gemm_w4a4(dev(A), dev(B), K, dev(sx), dev(sw), dev(b))).view(np.uint16)
+    want = oracle.f16_encode_rne_array(oracle.gemm_w4a4(A, B, K, sx, sw, b))
+    assert np.array_equal(got, want)
+
+
+def test_w4a4_strided_unaligned_and_k0():
+    """Row strides beyond K, operands at an odd byte offset (byte-gather
+    kernel), and K = 0 (Y = bias)."""
+    import torch
+    M, N, K = 70, 90, 160
+    A, B, sx, sw, b = inputs.w4a4_problem(M, N, K, seed=8)
+    Ab = np.zeros((M, K // 2 + 9), np.uint8); Ab[:, 1:1 + K // 2] = A
+    Bb = np.zeros((N, K // 2 + 9), np.uint8); Bb[:, 1:1 + K // 2] = B
+    got = host(mp.gemm_w4a4(dev(Ab)[:, 1:1 + K // 2], dev(Bb)[:, 1:1 + K // 2], K, dev(sx), dev(sw), dev(b)))
+    _w4a4_check(A, B, K, sx, sw, b, got, "w4a4 strided/unaligned")
+    z = host(mp.gemm_w4a4(dev(np.zeros((M, 0), np.uint8)), dev(np.zeros((N, 0), np.uint8)), 0,
+                          dev(sx), dev(sw), dev(b)))
+    assert np.array_equal(z.view(np.uint16), np.tile(b.view(np.uint16), (M, 1)))
+
+
+def test_w4a4_full_size_sampled_rows():
+    """N = 4096 and 8192: every row sampled is compared with the oracle."""
+    for n in (4096, 8192):
+        A, B, sx, sw, b = inputs.w4a4_problem(n, n, n, seed=n)
+        got = host(mp.gemm_w4a4(dev(A), dev(B), n, dev(sx), dev(sw), dev(b)))
+        rows = sample_rows(n, 12, seed=n)
+        _w4a4_check(A[rows], B, n, sx[rows], sw, b, got[rows], f"w4a4 {n} sampled rows")
+
+
 # ------------------------------------------------------------------ INT4 weight quantisation
 
 def _quant(W, G, h=None):
