@@ -176,6 +176,28 @@ mpgemm_status_t mpgemm_quantize_w4(mpgemm_handle_t h, int64_t N, int64_t K,
                                    uint8_t *Wq, int64_t ldwq, uint16_t *S, int64_t lds,
                                    void *stream);
 
+/* Precision tags of mpgemm_plan_gemm. */
+enum {
+    MPGEMM_PREC_F16 = 0,
+    MPGEMM_PREC_I8 = 1,
+    MPGEMM_PREC_I4 = 2,
+    MPGEMM_PREC_W4A4 = 3
+};
+
+/* Planning queries: which kernel configuration a call with these sizes runs
+ * on a device with cu_count compute units (with no configuration override),
+ * decided on the host from the sizes alone; no device is touched.
+ * mpgemm_plan_gemm: the tile configuration (the index the MPGEMM_TILE_CFG
+ * override takes) of mpgemm_run_{f16,i8,i4,w4a4}; operands that are not
+ * 16-byte aligned run the byte-gather kernel instead.
+ * mpgemm_plan_w4a16: the configuration of mpgemm_run_w4a16 (the index the
+ * MPGEMM_W4A16_CFG override takes), the number of workgroups K is split over
+ * (k_splits; 1 = no second reduction kernel) and the K extent of one split. */
+mpgemm_status_t mpgemm_plan_gemm(int precision, int64_t M, int64_t N, int64_t K, int cu_count,
+                                 int *config);
+mpgemm_status_t mpgemm_plan_w4a16(int64_t M, int64_t N, int64_t K, int cu_count, int *config,
+                                  int *k_splits, int64_t *k_slice);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,7 @@ __all__ = [
     "MpgemmError", "lib", "lib_path",
     "mpgemm_create", "mpgemm_destroy", "mpgemm_status_string",
     "mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_run_w4a4", "mpgemm_quantize_w4",
+    "mpgemm_plan_gemm", "mpgemm_plan_w4a16",
     "Handle", "default_handle", "gemm_f16", "gemm_i8", "gemm_i4", "gemm_w4a16", "gemm_w4a4", "quantize_w4",
 ]
 
@@ -64,6 +65,11 @@ def lib() -> ctypes.CDLL:
         L.mpgemm_run_w4a4.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
                                       _vp, _i64, _vp]
         L.mpgemm_run_w4a4.restype = ctypes.c_int
+        L.mpgemm_plan_gemm.argtypes = [ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        L.mpgemm_plan_gemm.restype = ctypes.c_int
+        L.mpgemm_plan_w4a16.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i64)]
+        L.mpgemm_plan_w4a16.restype = ctypes.c_int
         L.mpgemm_quantize_w4.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
         L.mpgemm_quantize_w4.restype = ctypes.c_int
         _lib = L
@@ -106,6 +112,20 @@ def mpgemm_run_w4a16(h, M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, st
 
 def mpgemm_run_w4a4(h, M, N, K, A, lda, B, ldb, SX, SW, bias, Y, ldy, stream=None) -> int:
     return lib().mpgemm_run_w4a4(h, M, N, K, A, lda, B, ldb, SX, SW, bias, Y, ldy, stream)
+
+
+def mpgemm_plan_gemm(precision, M, N, K, cu_count=256):
+    """(status, tile configuration) of a GEMM call; precision 0 f16, 1 i8, 2 i4, 3 w4a4."""
+    cfg = ctypes.c_int(-1)
+    st = lib().mpgemm_plan_gemm(precision, M, N, K, cu_count, ctypes.byref(cfg))
+    return st, cfg.value
+
+
+def mpgemm_plan_w4a16(M, N, K, cu_count=256):
+    """(status, configuration, K splits, K per split) of a weight-only call."""
+    cfg, ks, kslice = ctypes.c_int(-1), ctypes.c_int(0), ctypes.c_int64(0)
+    st = lib().mpgemm_plan_w4a16(M, N, K, cu_count, ctypes.byref(cfg), ctypes.byref(ks), ctypes.byref(kslice))
+    return st, cfg.value, ks.value, kslice.value
 
 
 def mpgemm_quantize_w4(h, N, K, W, ldw, group_size, Wq, ldwq, S, lds, stream=None) -> int:

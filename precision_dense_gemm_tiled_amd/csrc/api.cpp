@@ -71,22 +71,32 @@ mpgemm_status_t check_gemm(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K, c
 // Split-K workspace per handle: 32 MiB of fp32 partial sums.
 constexpr int64_t kSplitPartialFloats = int64_t(8) << 20;
 
-mpgemm_status_t bind_device(mpgemm_handle_t h) {
-    int cur = -1;
-    if (hipGetDevice(&cur) != hipSuccess)
-        return MPGEMM_ERR_HIP;
-    if (cur != h->device && hipSetDevice(h->device) != hipSuccess)
-        return MPGEMM_ERR_HIP;
-    return MPGEMM_OK;
-}
+// Makes the handle's device current for the duration of a call and restores
+// the caller's current device afterwards.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int device) {
+        if (hipGetDevice(&prev) != hipSuccess) {
+            prev = -1;
+            return;
+        }
+        ok = prev == device || hipSetDevice(device) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev)
+            (void)hipSetDevice(prev);
+    }
+};
 
 mpgemm_status_t run_tile(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int64_t kbytes,
                          const void *A, int64_t lda_b, const void *B, int64_t ldb_b, void *C,
                          int64_t ldc, void *stream, const uint16_t *sx = nullptr,
                          const uint16_t *sw = nullptr, const uint16_t *bias = nullptr) {
-    mpgemm_status_t st = bind_device(h);
-    if (st != MPGEMM_OK)
-        return st;
+    DeviceGuard dg(h->device);
+    if (!dg.ok)
+        return MPGEMM_ERR_HIP;
     mpg::GemmProblem p;
     p.A = static_cast<const uint8_t *>(A);
     p.B = static_cast<const uint8_t *>(B);
@@ -273,9 +283,9 @@ mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_
         return MPGEMM_ERR_UNSUPPORTED;
     if (!h)
         return MPGEMM_ERR_INVALID_ARG;
-    mpgemm_status_t st = bind_device(h);
-    if (st != MPGEMM_OK)
-        return st;
+    DeviceGuard dg(h->device);
+    if (!dg.ok)
+        return MPGEMM_ERR_HIP;
     mpg::W4A16Problem p;
     p.X = X;
     p.W = Wq;
@@ -289,8 +299,9 @@ mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_
     p.N = (int)N;
     p.K = (int)K;
     p.G = K > 0 ? (int)group_size : 32;
-    int cfg = h->forced_w4a16_cfg >= 0 ? h->forced_w4a16_cfg : mpg::choose_w4a16_cfg(M, N, K);
-    hipError_t e = mpg::launch_w4a16(p, cfg, h->ws, h->cu_count, static_cast<hipStream_t>(stream));
+    const int cfg = h->forced_w4a16_cfg >= 0 ? h->forced_w4a16_cfg : mpg::choose_w4a16_cfg(M, N, K);
+    const mpg::W4A16Plan plan = mpg::plan_w4a16(M, N, K, cfg, h->cu_count, h->ws.partial_floats);
+    hipError_t e = mpg::launch_w4a16(p, plan, h->ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
 }
 
@@ -317,9 +328,9 @@ mpgemm_status_t mpgemm_quantize_w4(mpgemm_handle_t h, int64_t N, int64_t K, cons
         return MPGEMM_ERR_UNSUPPORTED;
     if (!h)
         return MPGEMM_ERR_INVALID_ARG;
-    mpgemm_status_t st = bind_device(h);
-    if (st != MPGEMM_OK)
-        return st;
+    DeviceGuard dg(h->device);
+    if (!dg.ok)
+        return MPGEMM_ERR_HIP;
     mpg::QuantizeW4Problem p;
     p.W = W;
     p.Q = Wq;
@@ -332,4 +343,26 @@ mpgemm_status_t mpgemm_quantize_w4(mpgemm_handle_t h, int64_t N, int64_t K, cons
     p.G = (int)group_size;
     hipError_t e = mpg::launch_quantize_w4(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
+}
+
+mpgemm_status_t mpgemm_plan_gemm(int precision, int64_t M, int64_t N, int64_t K, int cu_count,
+                                 int *config) {
+    if (!config || M < 0 || N < 0 || K < 0 || cu_count < 1 || precision < MPGEMM_PREC_F16 ||
+        precision > MPGEMM_PREC_W4A4)
+        return MPGEMM_ERR_INVALID_ARG;
+    const int64_t kbytes = precision == MPGEMM_PREC_F16 ? 2 * K : (precision == MPGEMM_PREC_I8 ? K : K / 2);
+    *config = mpg::choose_tile_cfg(precision, M, N, kbytes, cu_count);
+    return MPGEMM_OK;
+}
+
+mpgemm_status_t mpgemm_plan_w4a16(int64_t M, int64_t N, int64_t K, int cu_count, int *config,
+                                  int *k_splits, int64_t *k_slice) {
+    if (!config || !k_splits || !k_slice || M < 1 || N < 1 || K < 0 || cu_count < 1)
+        return MPGEMM_ERR_INVALID_ARG;
+    const mpg::W4A16Plan plan =
+        mpg::plan_w4a16(M, N, K, mpg::choose_w4a16_cfg(M, N, K), cu_count, kSplitPartialFloats);
+    *config = plan.cfg;
+    *k_splits = plan.ks;
+    *k_slice = plan.ks > 1 ? plan.kslice : K;
+    return MPGEMM_OK;
 }

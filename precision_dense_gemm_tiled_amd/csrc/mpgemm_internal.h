@@ -87,7 +87,18 @@ struct W4A16Split {
 
 const char *w4a16_cfg_name(int cfg);
 int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K);
-hipError_t launch_w4a16(const W4A16Problem &p, int cfg, const W4A16Workspace &ws, int cu_count,
+
+// What a weight-only call runs, decided on the host from the sizes alone:
+// the configuration after fallbacks and, for the slice kernels, the split of
+// K over workgroups (ks slices of kslice k; ks = 1: no second kernel).
+struct W4A16Plan {
+    int cfg;
+    int ks;
+    int kslice;
+    int mblocks, ngroups;
+};
+W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cfg, int cu_count, int64_t partial_floats);
+hipError_t launch_w4a16(const W4A16Problem &p, const W4A16Plan &plan, const W4A16Workspace &ws,
                         hipStream_t stream);
 
 // Symmetric INT4 quantisation of fp16 weights per (row, G-wide K group).

@@ -611,38 +611,70 @@ static hipError_t launch_gemv(const W4A16Problem &p, hipStream_t stream, int lg)
 }
 
 template <int MB, int NB, int WN, int WK, int NST>
-static hipError_t launch_slice(const W4A16Problem &p, const W4A16Workspace &ws, int cu_count,
+static hipError_t launch_slice(const W4A16Problem &p, const W4A16Plan &plan, const W4A16Workspace &ws,
                                hipStream_t stream, int lg) {
-    constexpr int BM = 16 * MB, BN = 16 * NB * WN, KSPAN = 128 * NST * WK;
+    constexpr int BM = 16 * MB, BN = 16 * NB * WN;
     W4A16Split sk;
-    sk.mblocks = (p.M + BM - 1) / BM;
-    sk.ngroups = (p.N + BN - 1) / BN;
-    const int64_t tiles = (int64_t)sk.mblocks * sk.ngroups;
-    // K slices: at least K / KSPAN (what one workgroup holds), more while the
-    // grid would leave compute units idle
-    int ks = (p.K + KSPAN - 1) / KSPAN;
-    while (tiles * ks < cu_count && (int64_t)(ks + 1) * 128 <= p.K)
-        ++ks;
-    // equal slices in whole 128-k steps
-    const int steps = (p.K + 127) / 128;
-    const int spk = (steps + ks - 1) / ks;
-    ks = (steps + spk - 1) / spk;
-    if (ks > 1 && tiles * ks * BM * BN > ws.partial_floats)
-        return hipErrorOutOfMemory;   // caller falls back to a configuration without a workspace
-    sk.ks = ks;
-    sk.kslice = 128 * spk;
+    sk.mblocks = plan.mblocks;
+    sk.ngroups = plan.ngroups;
+    sk.ks = plan.ks;
+    sk.kslice = plan.kslice;
     sk.partial = ws.partial;
-    const int64_t blocks = tiles * ks;
+    const int64_t tiles = (int64_t)sk.mblocks * sk.ngroups;
+    const int64_t blocks = tiles * sk.ks;
     if (blocks > INT_MAX)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((w4a16_slice_kernel<MB, NB, WN, WK, NST>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        p, sk, lg);
-    if (ks == 1)
+    if (sk.ks == 1)
         return hipGetLastError();
     const int64_t total = tiles * BM * BN;
     hipLaunchKernelGGL((w4a16_reduce_kernel<MB, NB, WN>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                        stream, p, sk);
     return hipGetLastError();
+}
+
+// The slice configurations: (configuration, MB, NB, WN, WK, NST). One list
+// feeds both the host planning and the kernel dispatch.
+#define MPG_SLICE_CONFIGS(X)                 \
+    X(W4A16_SLICE_16x16_K4, 1, 1, 1, 4, 8)   \
+    X(W4A16_SLICE_32x32_K2, 2, 1, 2, 2, 8)   \
+    X(W4A16_SLICE_64x128, 4, 2, 4, 1, 8)     \
+    X(W4A16_SLICE_128x128, 8, 2, 4, 1, 4)
+
+W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cfg, int cu_count, int64_t partial_floats) {
+    W4A16Plan plan{K == 0 ? (int)W4A16_GEMV_R2_KS2 : cfg, 1, 0, 0, 0};
+    int MB = 0, NB = 0, WN = 0, WK = 0, NST = 0;
+    switch (plan.cfg) {
+#define MPG_SHAPE(C, mb, nb, wn, wk, nst) \
+    case C: MB = mb; NB = nb; WN = wn; WK = wk; NST = nst; break;
+        MPG_SLICE_CONFIGS(MPG_SHAPE)
+#undef MPG_SHAPE
+    default: return plan;   // GEMV and the older MFMA kernels split K inside the workgroup
+    }
+    const int64_t BM = 16 * MB, BN = 16 * NB * WN, KSPAN = 128 * NST * WK;
+    plan.mblocks = (int)((M + BM - 1) / BM);
+    plan.ngroups = (int)((N + BN - 1) / BN);
+    const int64_t tiles = (int64_t)plan.mblocks * plan.ngroups;
+    // K slices: at least K / KSPAN (what one workgroup holds), more while the
+    // grid would leave compute units idle
+    int64_t ks = (K + KSPAN - 1) / KSPAN;
+    while (tiles * ks < cu_count && (ks + 1) * 128 <= K)
+        ++ks;
+    // equal slices in whole 128-k steps
+    const int64_t steps = (K + 127) / 128;
+    const int64_t spk = (steps + ks - 1) / ks;
+    ks = (steps + spk - 1) / spk;
+    if (ks > 1 && tiles * ks * BM * BN > partial_floats) {
+        // the workspace cannot hold the partial tiles: a kernel that splits K
+        // inside its workgroups instead
+        plan.cfg = M <= 16 ? W4A16_MFMA_DECODE : W4A16_MFMA_TILE;
+        plan.mblocks = plan.ngroups = 0;
+        return plan;
+    }
+    plan.ks = (int)ks;
+    plan.kslice = (int)(128 * spk);
+    return plan;
 }
 
 const char *w4a16_cfg_name(int cfg) {
@@ -669,9 +701,9 @@ int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K) {
     return W4A16_SLICE_64x128;
 }
 
-static hipError_t launch_one(const W4A16Problem &p, int cfg, const W4A16Workspace &ws, int cu_count,
+static hipError_t launch_one(const W4A16Problem &p, const W4A16Plan &plan, const W4A16Workspace &ws,
                              hipStream_t stream, int lg) {
-    switch (cfg) {
+    switch (plan.cfg) {
     case W4A16_MFMA_DECODE: return launch_cfg<1, 1, 4, 8>(p, stream, lg);
     case W4A16_MFMA_TILE: return launch_cfg<2, 4, 1, 2>(p, stream, lg);
     case W4A16_GEMV_R1_KS2: return launch_gemv<1, 2>(p, stream, lg);
@@ -680,25 +712,20 @@ static hipError_t launch_one(const W4A16Problem &p, int cfg, const W4A16Workspac
     case W4A16_GEMV_R2_KS1: return launch_gemv<2, 1>(p, stream, lg);
     case W4A16_GEMV_R4_KS1: return launch_gemv<4, 1>(p, stream, lg);
     case W4A16_GEMV_R8_KS1: return launch_gemv<8, 1>(p, stream, lg);
-    case W4A16_SLICE_16x16_K4: return launch_slice<1, 1, 1, 4, 8>(p, ws, cu_count, stream, lg);
-    case W4A16_SLICE_32x32_K2: return launch_slice<2, 1, 2, 2, 8>(p, ws, cu_count, stream, lg);
-    case W4A16_SLICE_64x128: return launch_slice<4, 2, 4, 1, 8>(p, ws, cu_count, stream, lg);
-    case W4A16_SLICE_128x128: return launch_slice<8, 2, 4, 1, 4>(p, ws, cu_count, stream, lg);
+#define MPG_LAUNCH(C, mb, nb, wn, wk, nst) \
+    case C: return launch_slice<mb, nb, wn, wk, nst>(p, plan, ws, stream, lg);
+        MPG_SLICE_CONFIGS(MPG_LAUNCH)
+#undef MPG_LAUNCH
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_w4a16(const W4A16Problem &p, int cfg, const W4A16Workspace &ws, int cu_count,
+hipError_t launch_w4a16(const W4A16Problem &p, const W4A16Plan &plan, const W4A16Workspace &ws,
                         hipStream_t stream) {
     int lg = 0;
     while ((1 << lg) < p.G)
         ++lg;
-    if (p.K == 0)   // Y = 0: the GEMV writes zeros without touching the operands
-        cfg = W4A16_GEMV_R2_KS2;
-    hipError_t e = launch_one(p, cfg, ws, cu_count, stream, lg);
-    if (e == hipErrorOutOfMemory)   // split-K workspace too small for this shape
-        e = launch_one(p, p.M <= 16 ? W4A16_MFMA_DECODE : W4A16_MFMA_TILE, ws, cu_count, stream, lg);
-    return e;
+    return launch_one(p, plan, ws, stream, lg);
 }
 
 }  // namespace mpg

@@ -1,0 +1,103 @@
+"""Host-side planning of the library (no device): which tile configuration a
+GEMM runs and how a weight-only call splits K. These decide grid shapes and
+workspace use, so their invariants are checked here on many sizes."""
+import os
+
+import numpy as np
+import pytest
+
+OK, INVALID = 0, 1
+# slice configurations of the weight-only path: (BM, BN, K held by one workgroup)
+SLICE = {8: (16, 16, 4096), 9: (32, 32, 2048), 10: (64, 128, 1024), 11: (128, 128, 512)}
+WORKSPACE_FLOATS = 8 << 20
+
+
+@pytest.fixture(scope="module")
+def mp():
+    import precision_dense_gemm_tiled_amd as mp
+    if not os.path.exists(mp.lib_path):
+        from precision_dense_gemm_tiled_amd import build
+        build.build()
+    mp.lib()
+    return mp
+
+
+@pytest.mark.parametrize("prec", [0, 1, 2, 3])
+def test_tile_config_at_the_workload_sizes(mp, prec):
+    """Square sizes of the benchmark on 256 compute units: 64x64 tiles at 512
+    and 1024, 128x128 with a 4-stage ring at 2048, 256x256 from 4096 on."""
+    want = {512: 2, 1024: 2, 2048: 6, 4096: 4, 8192: 4}
+    for n, cfg in want.items():
+        assert mp.mpgemm_plan_gemm(prec, n, n, n, 256) == (OK, cfg), n
+
+
+def test_tile_config_fills_the_compute_units(mp):
+    """Whatever is chosen, the grid has at least half as many tiles as compute
+    units, or the smallest tile is chosen."""
+    tiles = {0: 256, 1: 128, 2: 64, 3: 256, 4: 256, 5: 128, 6: 128}   # BM (= BN for the square ones)
+    rng = np.random.default_rng(0)
+    for _ in range(500):
+        M, N, K = (int(v) for v in rng.integers(1, 20000, 3))
+        st, cfg = mp.mpgemm_plan_gemm(1, M, N, K, 256)
+        assert st == OK and cfg in (2, 3, 4, 6)
+        if cfg != 2:
+            bm = tiles[cfg]
+            bn = 128 if cfg == 3 else bm
+            assert -(-M // bm) * -(-N // bn) >= 128
+
+
+def test_plan_gemm_arguments(mp):
+    assert mp.mpgemm_plan_gemm(4, 8, 8, 8, 256)[0] == INVALID
+    assert mp.mpgemm_plan_gemm(0, -1, 8, 8, 256)[0] == INVALID
+    assert mp.mpgemm_plan_gemm(0, 8, 8, 8, 0)[0] == INVALID
+
+
+def test_w4a16_plan_at_the_workload_sizes(mp):
+    """N = K = 4096: GEMV for M = 1 (2 rows per wavefront) and M <= 4 (4 rows),
+    16 x 16 slices with K inside the workgroup at M = 16, 32 x 32 slices with K
+    split in 2 at M = 32 and 64, 64 x 128 slices with K split in 4 at M = 128."""
+    want = {1: (3, 1), 2: (4, 1), 4: (4, 1), 16: (8, 1), 32: (9, 2), 64: (9, 2), 128: (10, 4)}
+    for m, (cfg, ks) in want.items():
+        st, c, k, kslice = mp.mpgemm_plan_w4a16(m, 4096, 4096, 256)
+        assert (st, c, k) == (OK, cfg, ks), m
+        assert kslice == 4096 // ks
+
+
+def test_w4a16_plan_invariants(mp):
+    """Every split covers K with equal whole 128-k slices, none empty, none
+    longer than a workgroup holds, and the partial tiles fit the workspace;
+    otherwise the call falls back to a kernel without a split."""
+    rng = np.random.default_rng(1)
+    for _ in range(3000):
+        M = int(rng.integers(1, 3000))
+        N = int(rng.integers(1, 20000))
+        K = int(rng.integers(0, 40000)) // 32 * 32
+        st, cfg, ks, kslice = mp.mpgemm_plan_w4a16(M, N, K, 256)
+        assert st == OK
+        if K == 0:
+            assert cfg == 3 and ks == 1
+            continue
+        assert ks >= 1
+        if ks == 1:
+            assert kslice == K
+            continue
+        assert cfg in SLICE
+        bm, bn, span = SLICE[cfg]
+        assert kslice % 128 == 0 and kslice <= span
+        assert (ks - 1) * kslice < K <= ks * kslice
+        tiles = -(-M // bm) * -(-N // bn)
+        assert tiles * ks * bm * bn <= WORKSPACE_FLOATS
+
+
+def test_w4a16_plan_falls_back_when_the_workspace_is_too_small(mp):
+    """A very tall call whose partial tiles exceed the workspace runs the
+    K-inside-the-workgroup MFMA kernel instead (configuration 1)."""
+    st, cfg, ks, kslice = mp.mpgemm_plan_w4a16(4096, 16384, 16384, 256)
+    assert (st, ks) == (OK, 1) and cfg in (1, 10)
+    if cfg == 10:   # the slice kernel when no split is needed at all
+        assert kslice == 16384
+
+
+def test_plan_w4a16_arguments(mp):
+    assert mp.mpgemm_plan_w4a16(0, 8, 8, 256)[0] == INVALID
+    assert mp.mpgemm_plan_w4a16(8, 8, -8, 256)[0] == INVALID
