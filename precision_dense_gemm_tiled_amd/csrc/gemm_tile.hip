@@ -208,8 +208,6 @@ __device__ __forceinline__ void stage_factors(const GemmProblem &p, int row0, in
     __syncthreads();
 }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).
-// The LDS destination is wave-uniform: lane l writes lds + 16 * l.
 // Main kernel for 16-byte aligned operands whose BM (BN) rows span less than
 // 2^31 bytes. Full K tiles move from global memory straight into an NS-stage
 // LDS ring with direct-to-LDS loads (no staging registers, no ds_write),
@@ -245,7 +243,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // made explicitly uniform so the per-wavefront LDS bases live in scalar
+    // registers: the DMA destinations then need no per-copy readfirstlane
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / WGN) * WTM;
     const int wn0 = (wave % WGN) * WTN;
 
