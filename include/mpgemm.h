@@ -46,13 +46,17 @@
  *    boundary; such a read never crosses into another page.
  *  - Argument errors return before any HIP call and leave outputs untouched.
  *  - Output rows may not overlap inputs.
- *  - A handle owns 32 MiB of device memory, allocated by mpgemm_create and
- *    freed by mpgemm_destroy: the workspace where mpgemm_run_w4a16 keeps the
- *    fp32 partial sums of a K split. No call allocates memory.
- *  - mpgemm_run_{f16,i8,i4} calls may run concurrently on different streams
- *    with one handle. mpgemm_run_w4a16 calls that share a handle must not
- *    overlap in time (issue them on one stream, or use one handle per stream):
- *    they share its workspace.
+ *  - A handle owns 128 MiB + 64 KiB of device memory, allocated by
+ *    mpgemm_create and freed by mpgemm_destroy: the workspace where
+ *    mpgemm_run_w4a16 keeps the fp32 partial sums of a K split and where a
+ *    stream-K launch of mpgemm_run_{f16,i8,i4,w4a4} keeps partial tiles and
+ *    its per-tile arrival counters. No call allocates memory.
+ *  - Calls that share a handle must not overlap in time (issue them on one
+ *    stream, or use one handle per stream): they share its workspace. A
+ *    stream-K launch leaves its counters at zero when it completes; a launch
+ *    that never completes (a fault) leaves the handle unusable.
+ *  - Results do not depend on the schedule: stream-K partial tiles are summed
+ *    in a fixed order, so repeated calls give bit-identical outputs.
  */
 #ifndef MPGEMM_H
 #define MPGEMM_H
@@ -189,12 +193,17 @@ enum {
  * decided on the host from the sizes alone; no device is touched.
  * mpgemm_plan_gemm: the tile configuration (the index the MPGEMM_TILE_CFG
  * override takes) of mpgemm_run_{f16,i8,i4,w4a4}; operands that are not
- * 16-byte aligned run the byte-gather kernel instead.
+ * 16-byte aligned run the byte-gather kernel instead. sk_grid: 0 for a
+ * data-parallel launch (one workgroup per output tile), else the number of
+ * persistent workgroups of a stream-K launch, which runs the first
+ * sk_tiles_dp tiles whole and splits the K loops of the remaining tiles
+ * evenly over the grid (the MPGEMM_STREAMK=0/1 override turns it off, or on
+ * whenever the tiles do not fill whole waves of the grid).
  * mpgemm_plan_w4a16: the configuration of mpgemm_run_w4a16 (the index the
  * MPGEMM_W4A16_CFG override takes), the number of workgroups K is split over
  * (k_splits; 1 = no second reduction kernel) and the K extent of one split. */
 mpgemm_status_t mpgemm_plan_gemm(int precision, int64_t M, int64_t N, int64_t K, int cu_count,
-                                 int *config);
+                                 int *config, int *sk_grid, int *sk_tiles_dp);
 mpgemm_status_t mpgemm_plan_w4a16(int64_t M, int64_t N, int64_t K, int cu_count, int *config,
                                   int *k_splits, int64_t *k_slice);
 

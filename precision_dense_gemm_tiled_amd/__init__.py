@@ -65,7 +65,8 @@ def lib() -> ctypes.CDLL:
         L.mpgemm_run_w4a4.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
                                       _vp, _i64, _vp]
         L.mpgemm_run_w4a4.restype = ctypes.c_int
-        L.mpgemm_plan_gemm.argtypes = [ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        L.mpgemm_plan_gemm.argtypes = [ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                       ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
         L.mpgemm_plan_gemm.restype = ctypes.c_int
         L.mpgemm_plan_w4a16.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                         ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i64)]
@@ -115,10 +116,13 @@ def mpgemm_run_w4a4(h, M, N, K, A, lda, B, ldb, SX, SW, bias, Y, ldy, stream=Non
 
 
 def mpgemm_plan_gemm(precision, M, N, K, cu_count=256):
-    """(status, tile configuration) of a GEMM call; precision 0 f16, 1 i8, 2 i4, 3 w4a4."""
-    cfg = ctypes.c_int(-1)
-    st = lib().mpgemm_plan_gemm(precision, M, N, K, cu_count, ctypes.byref(cfg))
-    return st, cfg.value
+    """(status, tile configuration, stream-K grid (0: data-parallel), tiles run
+    whole before the stream-K part) of a GEMM call; precision 0 f16, 1 i8,
+    2 i4, 3 w4a4."""
+    cfg, grid, tdp = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_int(-1)
+    st = lib().mpgemm_plan_gemm(precision, M, N, K, cu_count, ctypes.byref(cfg), ctypes.byref(grid),
+                                ctypes.byref(tdp))
+    return st, cfg.value, grid.value, tdp.value
 
 
 def mpgemm_plan_w4a16(M, N, K, cu_count=256):

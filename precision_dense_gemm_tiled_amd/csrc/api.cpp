@@ -17,7 +17,12 @@ struct mpgemm_ctx {
     int cu_count;
     int forced_tile_cfg;   // -1: heuristic; else a TileCfg index (MPGEMM_TILE_CFG)
     int forced_w4a16_cfg;  // -1: heuristic; else a W4A16Cfg index (MPGEMM_W4A16_CFG)
-    mpg::W4A16Workspace ws; // split-K fp32 partial sums of the weight-only path (device memory)
+    int streamk_mode;      // mpg::StreamKMode (MPGEMM_STREAMK=0/1 forces it off/on)
+    // One device buffer of partial sums, used by the weight-only path's K
+    // split and by stream-K tile GEMMs (calls sharing a handle are serialized
+    // by the caller), and the stream-K arrival counters (zero between calls).
+    mpg::W4A16Workspace ws;
+    mpg::TileWorkspace tile_ws;
 };
 
 namespace {
@@ -68,8 +73,12 @@ mpgemm_status_t check_gemm(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K, c
     return h ? MPGEMM_OK : MPGEMM_ERR_INVALID_ARG;
 }
 
-// Split-K workspace per handle: 32 MiB of fp32 partial sums.
+// Partial-sum workspace per handle: 128 MiB (two 256 x 256 fp32 tiles per
+// compute unit for stream-K); the weight-only K split uses its first 32 MiB.
+constexpr int64_t kWorkspaceBytes = int64_t(128) << 20;
 constexpr int64_t kSplitPartialFloats = int64_t(8) << 20;
+// Stream-K arrival counters: one per split tile (at most two waves of tiles).
+constexpr int kStreamKFlags = 16384;
 
 // Makes the handle's device current for the duration of a call and restores
 // the caller's current device afterwards.
@@ -112,7 +121,10 @@ mpgemm_status_t run_tile(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int6
     p.bias = bias;
     int cfg = h->forced_tile_cfg >= 0 ? h->forced_tile_cfg
                                       : mpg::choose_tile_cfg(prec, M, N, kbytes, h->cu_count);
-    hipError_t e = mpg::launch_gemm(prec, cfg, p, static_cast<hipStream_t>(stream));
+    const mpg::StreamKPlan sk =
+        mpg::plan_stream_k(cfg, M, N, kbytes, h->cu_count, h->tile_ws.partial_bytes,
+                           h->tile_ws.flag_count, h->streamk_mode);
+    hipError_t e = mpg::launch_gemm(prec, cfg, p, sk, h->tile_ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
 }
 
@@ -156,13 +168,29 @@ mpgemm_status_t mpgemm_create(mpgemm_handle_t *out, int device) {
         if (v >= 0 && v < mpg::W4A16_CFG_COUNT)
             h->forced_w4a16_cfg = v;
     }
-    // Split-K workspace of the weight-only path (fp32 K slices of Y),
-    // allocated once here.
+    h->streamk_mode = mpg::SK_MODE_AUTO;
+    if (const char *env = std::getenv("MPGEMM_STREAMK")) {
+        if (env[0] == '0')
+            h->streamk_mode = mpg::SK_MODE_OFF;
+        else if (env[0] == '1')
+            h->streamk_mode = mpg::SK_MODE_ON;
+    }
+    // Workspace (partial sums of split K loops, stream-K arrival counters),
+    // allocated once here; the counters start at zero and every stream-K
+    // launch leaves them at zero.
     h->ws.partial = nullptr;
     h->ws.partial_floats = kSplitPartialFloats;
+    h->tile_ws.partial = nullptr;
+    h->tile_ws.partial_bytes = kWorkspaceBytes;
+    h->tile_ws.flags = nullptr;
+    h->tile_ws.flag_count = kStreamKFlags;
     int prev = -1;
     bool ok = hipGetDevice(&prev) == hipSuccess && hipSetDevice(device) == hipSuccess;
-    ok = ok && hipMalloc(reinterpret_cast<void **>(&h->ws.partial), kSplitPartialFloats * sizeof(float)) == hipSuccess;
+    ok = ok && hipMalloc(&h->tile_ws.partial, kWorkspaceBytes) == hipSuccess;
+    ok = ok && hipMalloc(reinterpret_cast<void **>(&h->tile_ws.flags), kStreamKFlags * sizeof(int)) == hipSuccess;
+    ok = ok && hipMemset(h->tile_ws.flags, 0, kStreamKFlags * sizeof(int)) == hipSuccess;
+    ok = ok && hipDeviceSynchronize() == hipSuccess;
+    h->ws.partial = static_cast<float *>(h->tile_ws.partial);
     if (prev >= 0)
         (void)hipSetDevice(prev);
     if (!ok) {
@@ -179,8 +207,10 @@ mpgemm_status_t mpgemm_destroy(mpgemm_handle_t h) {
     int prev = -1;
     (void)hipGetDevice(&prev);
     (void)hipSetDevice(h->device);
-    if (h->ws.partial)
-        (void)hipFree(h->ws.partial);
+    if (h->tile_ws.partial)
+        (void)hipFree(h->tile_ws.partial);
+    if (h->tile_ws.flags)
+        (void)hipFree(h->tile_ws.flags);
     if (prev >= 0)
         (void)hipSetDevice(prev);
     delete h;
@@ -346,12 +376,16 @@ mpgemm_status_t mpgemm_quantize_w4(mpgemm_handle_t h, int64_t N, int64_t K, cons
 }
 
 mpgemm_status_t mpgemm_plan_gemm(int precision, int64_t M, int64_t N, int64_t K, int cu_count,
-                                 int *config) {
-    if (!config || M < 0 || N < 0 || K < 0 || cu_count < 1 || precision < MPGEMM_PREC_F16 ||
-        precision > MPGEMM_PREC_W4A4)
+                                 int *config, int *sk_grid, int *sk_tiles_dp) {
+    if (!config || !sk_grid || !sk_tiles_dp || M < 0 || N < 0 || K < 0 || cu_count < 1 ||
+        precision < MPGEMM_PREC_F16 || precision > MPGEMM_PREC_W4A4)
         return MPGEMM_ERR_INVALID_ARG;
     const int64_t kbytes = precision == MPGEMM_PREC_F16 ? 2 * K : (precision == MPGEMM_PREC_I8 ? K : K / 2);
     *config = mpg::choose_tile_cfg(precision, M, N, kbytes, cu_count);
+    const mpg::StreamKPlan sk = mpg::plan_stream_k(*config, M, N, kbytes, cu_count, kWorkspaceBytes,
+                                                   kStreamKFlags, mpg::SK_MODE_AUTO);
+    *sk_grid = sk.grid;
+    *sk_tiles_dp = sk.tiles_dp;
     return MPGEMM_OK;
 }
 

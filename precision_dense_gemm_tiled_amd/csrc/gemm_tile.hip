@@ -31,9 +31,9 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-template <int P> struct AccOf { typedef i32x16 type; typedef int32_t out; };
-template <> struct AccOf<PREC_F16> { typedef f32x16 type; typedef float out; };
-template <> struct AccOf<PREC_W4A4> { typedef i32x16 type; typedef uint16_t out; };
+template <int P> struct AccOf { typedef i32x16 type; typedef int32_t out; typedef int elem; };
+template <> struct AccOf<PREC_F16> { typedef f32x16 type; typedef float out; typedef float elem; };
+template <> struct AccOf<PREC_W4A4> { typedef i32x16 type; typedef uint16_t out; typedef int elem; };
 
 // XOR swizzle of the 16-byte chunk position within an LDS row. Fragment reads
 // take one chunk column across 8 (or 16) consecutive rows; the swizzle spreads
@@ -49,26 +49,35 @@ __device__ __forceinline__ int swz(int row) {
         static_assert(CPR == 8 || CPR == 4, "unsupported LDS row width");
 }
 
-// Workgroup id -> output tile. Consecutive workgroup ids are dispatched
-// round-robin over the 8 XCDs, each with its own L2; give every XCD a
-// contiguous range of logical tiles, then walk the logical range in groups of
-// GROUP_M tile rows so concurrently running tiles share A rows and B rows.
-__device__ __forceinline__ void tile_of_block(int bid, int nblk, int tiles_m, int tiles_n,
-                                              int &tm, int &tn) {
-    constexpr int XCDS = 8, GROUP_M = 8;
-    int logical = bid;
-    if (nblk >= XCDS) {
-        int xcd = bid % XCDS, local = bid / XCDS;
-        int base = nblk / XCDS, rem = nblk % XCDS;
-        logical = xcd * base + (xcd < rem ? xcd : rem) + local;
-    }
-    int per_group = GROUP_M * tiles_n;
-    int group = logical / per_group;
-    int first_m = group * GROUP_M;
-    int gsize = tiles_m - first_m < GROUP_M ? tiles_m - first_m : GROUP_M;
-    int in_group = logical - group * per_group;
+// Consecutive workgroup ids are dispatched round-robin over the 8 XCDs, each
+// with its own L2: renumber them so every XCD holds a contiguous range of
+// logical ids.
+__device__ __forceinline__ int xcd_logical(int bid, int nblk) {
+    constexpr int XCDS = 8;
+    if (nblk < XCDS)
+        return bid;
+    const int xcd = bid % XCDS, local = bid / XCDS;
+    const int base = nblk / XCDS, rem = nblk % XCDS;
+    return xcd * base + (xcd < rem ? xcd : rem) + local;
+}
+
+// Logical tile index -> output tile: walk the tiles in groups of GROUP_M tile
+// rows so concurrently running tiles share A rows and B rows in L2.
+__device__ __forceinline__ void tile_raster(int logical, int tiles_m, int tiles_n, int &tm, int &tn) {
+    constexpr int GROUP_M = 8;
+    const int per_group = GROUP_M * tiles_n;
+    const int group = logical / per_group;
+    const int first_m = group * GROUP_M;
+    const int gsize = tiles_m - first_m < GROUP_M ? tiles_m - first_m : GROUP_M;
+    const int in_group = logical - group * per_group;
     tm = first_m + in_group % gsize;
     tn = in_group / gsize;
+}
+
+// Workgroup id -> output tile when the grid has one workgroup per tile.
+__device__ __forceinline__ void tile_of_block(int bid, int nblk, int tiles_m, int tiles_n,
+                                              int &tm, int &tn) {
+    tile_raster(xcd_logical(bid, nblk), tiles_m, tiles_n, tm, tn);
 }
 
 // Zero the bytes of a 16-byte chunk at positions >= nvalid (0 <= nvalid <= 16).
@@ -208,183 +217,351 @@ __device__ __forceinline__ void stage_factors(const GemmProblem &p, int row0, in
     __syncthreads();
 }
 
-// Main kernel for 16-byte aligned operands whose BM (BN) rows span less than
-// 2^31 bytes. Full K tiles move from global memory straight into an NS-stage
-// LDS ring with direct-to-LDS loads (no staging registers, no ds_write),
-// NS - 1 tiles ahead of the MFMAs that consume them. One load instruction of
-// a wavefront fills 1 KiB of contiguous LDS, i.e. 64 / CPR whole rows of a
-// tile; lane l lands at row l / CPR, 16-byte slot l % CPR, so it fetches the
-// global chunk that the XOR swizzle puts in that slot. Each thread's rows are
-// r0 + i * RS (RS = NT / CPR), whose swizzle is the same for every i, so its
-// addresses are one uniform block base plus one 32-bit offset per load.
+// Main loop for 16-byte aligned operands whose BM (BN) rows span less than
+// 2^31 bytes: accumulates pipeline entries [e0, e1) of output tile
+// (row0, col0) into acc. Full K tiles move from global memory straight into
+// an NS-stage LDS ring with direct-to-LDS loads (no staging registers, no
+// ds_write), NS - 1 tiles ahead of the MFMAs that consume them. One load
+// instruction of a wavefront fills 1 KiB of contiguous LDS, i.e. 64 / CPR
+// whole rows of a tile; lane l lands at row l / CPR, 16-byte slot l % CPR, so
+// it fetches the global chunk that the XOR swizzle puts in that slot. Each
+// thread's rows are r0 + i * RS (RS = NT / CPR), whose swizzle is the same for
+// every i, so its addresses are one uniform block base plus one 32-bit offset
+// per load.
+//
+// Entries: if K is not a multiple of BKB, entry 0 is the partial K tile
+// (loaded through registers with K masking); entry e >= NPRE is full K tile
+// e - NPRE. The caller guarantees 0 <= e0 < e1 <= KT and that the ring is
+// free (no wavefront still reads it). On return every load has landed.
 template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p, int tiles_m,
-                                                                   int tiles_n) {
-    constexpr int NT = 64 * WGM * WGN;
-    constexpr int WTM = BM / WGM, WTN = BN / WGN;
-    constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int CPR = BKB / 16;
-    constexpr int RS = NT / CPR;
-    constexpr int A_PER_T = BM / RS, B_PER_T = BN / RS;
-    constexpr int NL = A_PER_T + B_PER_T;   // direct-to-LDS loads per thread per tile
-    constexpr int STAGE = (BM + BN) * BKB;
-    constexpr int STEPS = CPR / 2;
+struct RingTile {
+    static constexpr int NT = 64 * WGM * WGN;
+    static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static constexpr int CPR = BKB / 16;
+    static constexpr int RS = NT / CPR;
+    static constexpr int A_PER_T = BM / RS, B_PER_T = BN / RS;
+    static constexpr int NL = A_PER_T + B_PER_T;   // direct-to-LDS loads per thread per tile
+    static constexpr int STAGE = (BM + BN) * BKB;
+    static constexpr int STEPS = CPR / 2;
+    static constexpr int LDS_BYTES = NS * STAGE;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
     static_assert(NT % CPR == 0 && BM % RS == 0 && BN % RS == 0, "staging must divide evenly");
     static_assert(RS % 16 == 0, "swizzle must repeat every RS rows");
     static_assert(STEPS % 2 == 0, "k-steps per stage alternate two fragment buffers");
     static_assert(NS >= 2 && (NS - 2) * NL < 64, "ring depth");
     // LDS budget, checked at build time (160 KiB per workgroup on gfx950).
-    static_assert(NS * STAGE <= 160 * 1024, "LDS ring exceeds 160 KiB");
-
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
     typedef typename AccOf<P>::type acc_t;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
+    static __device__ __forceinline__ void mainloop(const GemmProblem &p, uint8_t *smem, int row0,
+                                                    int col0, int e0, int e1, int tid, int lane,
+                                                    int wave, acc_t (&acc)[TM][TN]) {
+        const int wm0 = (wave / WGN) * WTM;
+        const int wn0 = (wave % WGN) * WTN;
+        const int64_t kbytes = p.kbytes;
+        const int KF = (int)(kbytes / BKB);     // full K tiles
+        const bool tail = (kbytes % BKB) != 0;  // plus one partial tile
+        const int NPRE = tail ? 1 : 0;
+
+        const int r0 = tid / CPR;
+        const int cg = (tid % CPR) ^ swz<CPR>(r0);   // global chunk of this lane's slot
+        const uint8_t *Ab = p.A + (int64_t)row0 * p.lda_b;
+        const uint8_t *Bb = p.B + (int64_t)col0 * p.ldb_b;
+        const int a_rows = p.M - row0, b_rows = p.N - col0;   // >= 1
+        uint32_t off[NL];
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i) {
+            int r = r0 + i * RS;
+            r = r < a_rows ? r : a_rows - 1;   // clamped rows feed outputs never stored
+            off[i] = (uint32_t)r * (uint32_t)p.lda_b + cg * 16;
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER_T; ++i) {
+            int r = r0 + i * RS;
+            r = r < b_rows ? r : b_rows - 1;
+            off[A_PER_T + i] = (uint32_t)r * (uint32_t)p.ldb_b + cg * 16;
+        }
+        // wave-uniform LDS base of this wavefront's DMA rows within a stage
+        const int wrow = wave * (64 / CPR);
+
+        // Every call issues exactly NL loads (entries past the last full tile
+        // re-read it into a stage that is free), so a fixed vmcnt tells which
+        // entry has landed. The host sends problems with no full K tile
+        // (KF == 0) to the generic kernel.
+        auto dma_entry = [&](int e) {
+            int kt = e - NPRE;
+            kt = kt < KF - 1 ? kt : KF - 1;
+            const uint8_t *a = Ab + (int64_t)kt * BKB;
+            const uint8_t *b = Bb + (int64_t)kt * BKB;
+            uint8_t *S = smem + (e % NS) * STAGE + wrow * BKB;
+#pragma unroll
+            for (int i = 0; i < A_PER_T; ++i)
+                dma16(a + off[i], S + i * RS * BKB);
+#pragma unroll
+            for (int i = 0; i < B_PER_T; ++i)
+                dma16(b + off[A_PER_T + i], S + BM * BKB + i * RS * BKB);
+        };
+        // partial tile kt -> stage 0 through registers, bytes past K cleared
+        auto reg_tail = [&](int kt) {
+            const int64_t k0 = (int64_t)kt * BKB + cg * 16;
+            uint8_t *S = smem + r0 * BKB + ((tid % CPR) * 16);
+#pragma unroll
+            for (int i = 0; i < A_PER_T; ++i) {
+                const i32x4 v = load_chunk_masked(Ab + (off[i] - cg * 16), k0, kbytes, r0 + i * RS < a_rows);
+                *reinterpret_cast<i32x4 *>(S + i * RS * BKB) = v;
+            }
+#pragma unroll
+            for (int i = 0; i < B_PER_T; ++i) {
+                const i32x4 v = load_chunk_masked(Bb + (off[A_PER_T + i] - cg * 16), k0, kbytes,
+                                                  r0 + i * RS < b_rows);
+                *reinterpret_cast<i32x4 *>(S + BM * BKB + i * RS * BKB) = v;
+            }
+        };
+
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = acc_t{};
+
+        // Prologue: entries e0 .. e0 + NS - 2 in flight; wait for entry e0 only.
+        i32x4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+        if (tail && e0 == 0)
+            reg_tail(KF);
+        else
+            dma_entry(e0);
+#pragma unroll
+        for (int e = 1; e < NS - 1; ++e)
+            dma_entry(e0 + e);
+        // entry e0 has landed (through LDS DMA, or through registers: lgkmcnt)
+        wait_vm_lds<(NS - 2) * NL>();
+        lds_barrier();
+        read_frags<BM, BKB, TM, TN>(smem + (e0 % NS) * STAGE, 0, wm0, wn0, lane, fa0, fb0);
+
+        // One pipeline entry e in LDS stage e % NS. Region A (before the
+        // barrier): the direct-to-LDS loads of entry e + NS - 1 into the stage
+        // freed by entry e - 1; per k-step, the fragment reads of the next step
+        // and the MFMAs of this one; the first KA MFMAs of the last step. The
+        // barrier publishes entry e + 1 (its loads, issued NS - 2 entries
+        // earlier, are the oldest ones outstanding) and certifies that every
+        // wavefront has finished reading stage e % NS. Region B: step-0
+        // fragment reads of the next stage interleaved with the rest of the
+        // last step's MFMAs.
+        constexpr int NMF = TM * TN;
+        constexpr int KA = NMF >= 4 ? NMF / 4 : 1;
+        for (int e = e0; e < e1; ++e) {
+            const uint8_t *S = smem + (e % NS) * STAGE;
+            const uint8_t *Snext = smem + ((e + 1) % NS) * STAGE;
+            __builtin_amdgcn_sched_barrier(0);
+            dma_entry(e + NS - 1);
+#pragma unroll
+            for (int step = 0; step < STEPS - 1; ++step) {
+                // one scheduling region per k-step: fragment reads of the next
+                // step and the MFMAs of this one (no back-to-back MFMAs on one
+                // accumulator across steps)
+                if (step % 2 == 0) {
+                    read_frags<BM, BKB, TM, TN>(S, step + 1, wm0, wn0, lane, fa1, fb1);
+                    mfma_step<P, TM, TN>(fa0, fb0, acc);
+                } else {
+                    read_frags<BM, BKB, TM, TN>(S, step + 1, wm0, wn0, lane, fa0, fb0);
+                    mfma_step<P, TM, TN>(fa1, fb1, acc);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            mfma_step<P, TM, TN, 0, KA>(fa1, fb1, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm_lds<(NS - 2) * NL>();
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags<BM, BKB, TM, TN>(Snext, 0, wm0, wn0, lane, fa0, fb0);
+            mfma_step<P, TM, TN, KA, NMF>(fa1, fb1, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the last entries' dummy loads must land before the ring is reused
+        wait_vm_lds<0>();
+    }
+
+    // Output of a finished tile: C for the plain GEMMs; for W4A4 the scale
+    // epilogue with the factors staged in the (then free) LDS ring.
+    static __device__ __forceinline__ void epilogue(const GemmProblem &p, uint8_t *smem, int row0,
+                                                    int col0, int tid, int lane, int wave,
+                                                    const acc_t (&acc)[TM][TN]) {
+        const int wm0 = (wave / WGN) * WTM;
+        const int wn0 = (wave % WGN) * WTN;
+        if constexpr (P == PREC_W4A4) {
+            static_assert((BM + 2 * BN) * 4 <= LDS_BYTES, "factor staging fits the ring");
+            float *fac = reinterpret_cast<float *>(smem);
+            stage_factors<BM, BN, NT>(p, row0, col0, tid, fac);
+            store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc, fac + wm0, fac + BM + wn0,
+                                  fac + BM + BN + wn0);
+        } else {
+            store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc);
+        }
+    }
+};
+
+// Data-parallel kernel: one output tile per workgroup, all of K.
+template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p, int tiles_m,
+                                                                   int tiles_n) {
+    typedef RingTile<P, BM, BN, BKB, WGM, WGN, NS> RT;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[RT::LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // made explicitly uniform so the per-wavefront LDS bases live in scalar
     // registers: the DMA destinations then need no per-copy readfirstlane
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm0 = (wave / WGN) * WTM;
-    const int wn0 = (wave % WGN) * WTN;
 
     int tm, tn;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
     const int row0 = tm * BM, col0 = tn * BN;
+    const int KT = (int)((p.kbytes + BKB - 1) / BKB);
 
-    const int64_t kbytes = p.kbytes;
-    const int KF = (int)(kbytes / BKB);     // full K tiles
-    const bool tail = (kbytes % BKB) != 0;  // plus one partial tile
-    // Entry 0 is the partial tile if there is one (loaded through registers
-    // with K masking in the prologue); the full tiles follow.
-    const int KT = KF + (tail ? 1 : 0);
-    const int NPRE = tail ? 1 : 0;
+    typename RT::acc_t acc[RT::TM][RT::TN];
+    RT::mainloop(p, smem, row0, col0, 0, KT, tid, lane, wave, acc);
+    RT::epilogue(p, smem, row0, col0, tid, lane, wave, acc);
+}
 
-    const int r0 = tid / CPR;
-    const int cg = (tid % CPR) ^ swz<CPR>(r0);   // global chunk of this lane's slot
-    const uint8_t *Ab = p.A + (int64_t)row0 * p.lda_b;
-    const uint8_t *Bb = p.B + (int64_t)col0 * p.ldb_b;
-    const int a_rows = p.M - row0, b_rows = p.N - col0;   // >= 1
-    uint32_t off[NL];
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-        int r = r0 + i * RS;
-        r = r < a_rows ? r : a_rows - 1;   // clamped rows feed outputs never stored
-        off[i] = (uint32_t)r * (uint32_t)p.lda_b + cg * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) {
-        int r = r0 + i * RS;
-        r = r < b_rows ? r : b_rows - 1;
-        off[A_PER_T + i] = (uint32_t)r * (uint32_t)p.ldb_b + cg * 16;
-    }
-    // wave-uniform LDS base of this wavefront's DMA rows within a stage
-    const int wrow = wave * (64 / CPR);
+// Stream-K partial accumulators: 16-byte loads and stores that are coherent
+// across the XCDs' L2 caches (sc1: written through, read past a stale line),
+// so that no cache-wide write-back or invalidation is needed.
+__device__ __forceinline__ void sk_store16(__amdgpu_buffer_rsrc_t r, int off, i32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 16);
+}
+__device__ __forceinline__ i32x4 sk_load16(__amdgpu_buffer_rsrc_t r, int off) {
+    // the builtin's own 16-byte vector type; converting it implicitly to
+    // i32x4 would narrow the load to its first dword
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
+    return __builtin_bit_cast(i32x4, v);
+}
 
-    // Entry e (> NPRE - 1) is full tile e - NPRE. Every call issues exactly
-    // NL loads (entries past the end re-read the last full tile into a stage
-    // that is free), so a fixed vmcnt tells which entry has landed. The host
-    // sends problems with no full K tile (KF == 0) to the generic kernel.
-    auto dma_entry = [&](int e) {
-        int kt = e - NPRE;
-        kt = kt < KF - 1 ? kt : KF - 1;
-        const uint8_t *a = Ab + (int64_t)kt * BKB;
-        const uint8_t *b = Bb + (int64_t)kt * BKB;
-        uint8_t *S = smem + (e % NS) * STAGE + wrow * BKB;
-#pragma unroll
-        for (int i = 0; i < A_PER_T; ++i)
-            dma16(a + off[i], S + i * RS * BKB);
-#pragma unroll
-        for (int i = 0; i < B_PER_T; ++i)
-            dma16(b + off[A_PER_T + i], S + BM * BKB + i * RS * BKB);
-    };
-    // partial tile kt -> stage 0 through registers, bytes past K cleared
-    auto reg_tail = [&](int kt) {
-        const int64_t k0 = (int64_t)kt * BKB + cg * 16;
-        uint8_t *S = smem + r0 * BKB + ((tid % CPR) * 16);
-#pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) {
-            const i32x4 v = load_chunk_masked(Ab + (off[i] - cg * 16), k0, kbytes, r0 + i * RS < a_rows);
-            *reinterpret_cast<i32x4 *>(S + i * RS * BKB) = v;
-        }
-#pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) {
-            const i32x4 v = load_chunk_masked(Bb + (off[A_PER_T + i] - cg * 16), k0, kbytes,
-                                              r0 + i * RS < b_rows);
-            *reinterpret_cast<i32x4 *>(S + BM * BKB + i * RS * BKB) = v;
-        }
-    };
+// Workgroup whose stream-K range holds iteration x (ranges [w I / G, (w+1) I / G)).
+__device__ __forceinline__ int sk_owner(int64_t x, int64_t iters, int grid) {
+    return (int)(((x + 1) * grid - 1) / iters);
+}
+
+// Stream-K kernel ("Stream-K" work decomposition, the persistent tile
+// scheduling that the L4 study names as next step): a persistent grid of G
+// workgroups first runs tiles [0, tiles_dp) whole (round-robin), then splits
+// the K iterations of the remaining tiles evenly: workgroup w runs iterations
+// [w I / G, (w+1) I / G), tile by tile. A tile whose iterations span several
+// workgroups is finished by the last of them to arrive: each contributor
+// stores its partial accumulators (coherent stores), waits for them to
+// complete and increments the tile's counter; the one that sees all others
+// done sums the contributions in workgroup order (its own from registers),
+// writes the output and resets the counter to zero. Nobody waits on another
+// workgroup, and the summation order does not depend on arrival order.
+template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_sk_kernel(GemmProblem p, int tiles_m,
+                                                                      int tiles_n, StreamKArgs sk) {
+    typedef RingTile<P, BM, BN, BKB, WGM, WGN, NS> RT;
+    typedef typename RT::acc_t acc_t;
+    constexpr int TM = RT::TM, TN = RT::TN, NT = RT::NT;
+    constexpr int SLOT = BM * BN * 4;   // bytes of one partial tile
+    typedef typename AccOf<P>::elem elem4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) uint8_t smem[RT::LDS_BYTES];
+    __shared__ int sk_flag;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = gridDim.x;
+    const int w = xcd_logical(blockIdx.x, G);
+    const int KT = (int)((p.kbytes + BKB - 1) / BKB);
 
     acc_t acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            acc[i][j] = acc_t{};
-
-    // Prologue: entries 0 .. NS-2 in flight; wait for entry 0 only.
-    i32x4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-    if (tail)
-        reg_tail(KF);
-    else
-        dma_entry(0);
-#pragma unroll
-    for (int e = 1; e < NS - 1; ++e)
-        dma_entry(e);
-    // entry 0 has landed (through LDS DMA, or through registers: lgkmcnt)
-    wait_vm_lds<(NS - 2) * NL>();
-    lds_barrier();
-    read_frags<BM, BKB, TM, TN>(smem, 0, wm0, wn0, lane, fa0, fb0);
-
-    // One pipeline entry e in LDS stage e % NS. Region A (before the
-    // barrier): the direct-to-LDS loads of entry e + NS - 1 into the stage
-    // freed by entry e - 1; per k-step, the fragment reads of the next step
-    // and the MFMAs of this one; the first KA MFMAs of the last step. The barrier publishes entry e + 1 (its
-    // loads, issued NS - 2 entries earlier, are the oldest ones outstanding)
-    // and certifies that every wavefront has finished reading stage e % NS.
-    // Region B: step-0 fragment reads of the next stage interleaved with the
-    // rest of the last step's MFMAs.
-    constexpr int NMF = TM * TN;
-    constexpr int KA = NMF >= 4 ? NMF / 4 : 1;
-    for (int e = 0; e < KT; ++e) {
-        const uint8_t *S = smem + (e % NS) * STAGE;
-        const uint8_t *Snext = smem + ((e + 1) % NS) * STAGE;
-        __builtin_amdgcn_sched_barrier(0);
-        dma_entry(e + NS - 1);
-#pragma unroll
-        for (int step = 0; step < STEPS - 1; ++step) {
-            // one scheduling region per k-step: fragment reads of the next
-            // step, then the MFMAs of this one (no back-to-back MFMAs on one
-            // accumulator across steps)
-            if (step % 2 == 0) {
-                read_frags<BM, BKB, TM, TN>(S, step + 1, wm0, wn0, lane, fa1, fb1);
-                mfma_step<P, TM, TN>(fa0, fb0, acc);
-            } else {
-                read_frags<BM, BKB, TM, TN>(S, step + 1, wm0, wn0, lane, fa0, fb0);
-                mfma_step<P, TM, TN>(fa1, fb1, acc);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        mfma_step<P, TM, TN, 0, KA>(fa1, fb1, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm_lds<(NS - 2) * NL>();
-        lds_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags<BM, BKB, TM, TN>(Snext, 0, wm0, wn0, lane, fa0, fb0);
-        mfma_step<P, TM, TN, KA, NMF>(fa1, fb1, acc);
-        __builtin_amdgcn_sched_barrier(0);
+    int tm, tn;
+    for (int t = w; t < sk.tiles_dp; t += G) {
+        tile_raster(t, tiles_m, tiles_n, tm, tn);
+        RT::mainloop(p, smem, tm * BM, tn * BN, 0, KT, tid, lane, wave, acc);
+        RT::epilogue(p, smem, tm * BM, tn * BN, tid, lane, wave, acc);
+        __syncthreads();   // the ring is free again
     }
-    // the last entries' dummy loads must land before the wavefront exits
-    wait_vm_lds<0>();
-    if constexpr (P == PREC_W4A4) {
-        static_assert((BM + 2 * BN) * 4 <= NS * STAGE, "factor staging fits the ring");
-        float *fac = reinterpret_cast<float *>(smem);
-        stage_factors<BM, BN, NT>(p, row0, col0, tid, fac);
-        store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc, fac + wm0, fac + BM + wn0,
-                              fac + BM + BN + wn0);
-    } else {
-        store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc);
+
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(sk.partial, 0, sk.partial_bytes, 0x00020000);
+    const int64_t I = sk.iters;
+    const int64_t beg = I * w / G, end = I * (w + 1) / G;
+    for (int64_t it = beg; it < end;) {
+        const int tl = (int)(it / KT);
+        const int e0 = (int)(it - (int64_t)tl * KT);
+        const int e1 = (int)((int64_t)KT - e0 < end - it ? KT : e0 + (end - it));
+        tile_raster(sk.tiles_dp + tl, tiles_m, tiles_n, tm, tn);
+        const int row0 = tm * BM, col0 = tn * BN;
+        RT::mainloop(p, smem, row0, col0, e0, e1, tid, lane, wave, acc);
+        bool finish = e0 == 0 && e1 == KT;
+        if (!finish) {
+            const int64_t t0 = (int64_t)tl * KT;
+            const int w_lo = sk_owner(t0, I, G), w_hi = sk_owner(t0 + KT - 1, I, G);
+            const int n = w_hi - w_lo + 1;
+            // slot 0: the tile where a workgroup's range starts (floor(I v / G)
+            // >= t0, i.e. I v >= t0 G); slot 1: the other one
+            auto slot_off = [&](int v) {
+                const bool first = I * v >= t0 * G;
+                return (2 * v + (first ? 0 : 1)) * SLOT;
+            };
+            if (tid == 0)
+                sk_flag = __hip_atomic_load(sk.flags + tl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            finish = sk_flag == n - 1;   // every other contributor is done already
+            if (!finish) {
+                const int base = slot_off(w);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            // whole vectors are bit-cast (never a vector element)
+                            const elem4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                             acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                            sk_store16(rs, base + (((i * TN + j) * 4 + q) * NT + tid) * 16,
+                                       __builtin_bit_cast(i32x4, v));
+                        }
+                // stores complete (written through) before the counter moves
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(0);
+                asm volatile("" ::: "memory");
+                __syncthreads();
+                if (tid == 0)
+                    sk_flag = __hip_atomic_fetch_add(sk.flags + tl, 1, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+                finish = sk_flag == n - 1;
+            }
+            if (finish) {
+                // sum of the contributions in workgroup order
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        acc_t sum = acc[i][j];
+                        for (int v = w_lo; v <= w_hi; ++v) {
+                            acc_t c = acc[i][j];
+                            if (v != w) {
+                                const int base = slot_off(v);
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    const elem4 x = __builtin_bit_cast(
+                                        elem4, sk_load16(rs, base + (((i * TN + j) * 4 + q) * NT + tid) * 16));
+#pragma unroll
+                                    for (int d = 0; d < 4; ++d)
+                                        c[4 * q + d] = x[d];
+                                }
+                            }
+                            sum = v == w_lo ? c : sum + c;
+                        }
+                        acc[i][j] = sum;
+                    }
+                if (tid == 0)
+                    __hip_atomic_store(sk.flags + tl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        if (finish)
+            RT::epilogue(p, smem, row0, col0, tid, lane, wave, acc);
+        __syncthreads();   // the ring (and sk_flag) are free again
+        it += e1 - e0;
     }
 }
 
@@ -477,20 +654,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_generic_kernel(GemmP
 
 // ------------------------------------------------------------------ launch
 
-struct CfgShape { int BM, BN; const char *name; };
+// BM x BN tile, BKB bytes of K per stage, blocks that one compute unit holds
+// at once (LDS: NS * (BM + BN) * BKB bytes each, 160 KiB per CU).
+struct CfgShape { int BM, BN, BKB, per_cu; const char *name; };
 static const CfgShape kCfg[CFG_COUNT] = {
-    {256, 256, "256x256_bk64_ring4"},
-    {128, 128, "128x128_bk64_ring4"},
-    {64, 64, "64x64_bk128_ring3"},
-    {256, 128, "256x128_bk128_ring3"},
-    {256, 256, "256x256_bk128_ring2"},
-    {128, 256, "128x256_bk128_ring3"},
-    {128, 128, "128x128_bk128_ring4"},
-    {256, 256, "256x256_bk128_ring2_w8"},
-    {256, 256, "256x256_bk64_ring4_w8"},
-    {256, 128, "256x128_bk64_ring3_2blk"},
-    {128, 128, "128x128_bk128_ring2_2blk"},
-    {128, 256, "128x256_bk64_ring3_2blk"},
+    {256, 256, 64, 1, "256x256_bk64_ring4"},
+    {128, 128, 64, 2, "128x128_bk64_ring4"},
+    {64, 64, 128, 3, "64x64_bk128_ring3"},
+    {256, 128, 128, 1, "256x128_bk128_ring3"},
+    {256, 256, 128, 1, "256x256_bk128_ring2"},
+    {128, 256, 128, 1, "128x256_bk128_ring3"},
+    {128, 128, 128, 1, "128x128_bk128_ring4"},
+    {256, 256, 128, 1, "256x256_bk128_ring2_w8"},
+    {256, 256, 64, 1, "256x256_bk64_ring4_w8"},
+    {256, 128, 64, 2, "256x128_bk64_ring3_2blk"},
+    {128, 128, 128, 2, "128x128_bk128_ring2_2blk"},
+    {128, 256, 64, 2, "128x256_bk64_ring3_2blk"},
 };
 
 const char *tile_cfg_name(int cfg) {
@@ -515,17 +694,71 @@ int choose_tile_cfg(int prec, int64_t M, int64_t N, int64_t kbytes, int cu_count
     return CFG_64x64;
 }
 
+StreamKPlan plan_stream_k(int cfg, int64_t M, int64_t N, int64_t kbytes, int cu_count,
+                          int64_t partial_bytes, int flag_count, int mode) {
+    StreamKPlan pl = {0, 0, 0, 0};
+    if (mode == SK_MODE_OFF || cfg < 0 || cfg >= CFG_COUNT || cu_count < 1)
+        return pl;
+    const CfgShape &c = kCfg[cfg];
+    const int64_t KT = (kbytes + c.BKB - 1) / c.BKB;
+    if (kbytes < c.BKB || KT < 2)   // the generic kernel, or nothing to split
+        return pl;
+    const int64_t T = ((M + c.BM - 1) / c.BM) * ((N + c.BN - 1) / c.BN);
+    const int64_t G = (int64_t)cu_count * c.per_cu;   // workgroups resident at once
+    const int64_t full = T / G, rem = T % G;
+    if (rem == 0)
+        return pl;   // whole waves: nothing to balance
+    if (mode == SK_MODE_AUTO) {
+        // Split only a short last wave of a grid of at least one full wave:
+        // the split tiles then cost one partial-tile round trip each, against
+        // a last wave that would leave most compute units idle.
+        if (full < 1 || rem * 2 > G)
+            return pl;
+    }
+    // The last full wave joins the stream-K part, so every workgroup runs
+    // between 1 and 2 tiles of iterations there ("two-tile" hybrid).
+    const int64_t tiles_dp = full >= 1 ? (full - 1) * G : 0;
+    const int64_t sk_tiles = T - tiles_dp;
+    const int64_t iters = sk_tiles * KT;
+    const int64_t grid = iters < G ? iters : G;
+    const int64_t need = 2 * grid * (int64_t)c.BM * c.BN * 4;
+    if (need > partial_bytes || need > INT32_MAX || sk_tiles > flag_count || tiles_dp > INT32_MAX)
+        return pl;
+    pl.grid = (int)grid;
+    pl.tiles_dp = (int)tiles_dp;
+    pl.sk_tiles = (int)sk_tiles;
+    pl.iters = iters;
+    return pl;
+}
+
 template <int P>
 static hipError_t launch_generic(const GemmProblem &p, hipStream_t stream);
 
 template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS>
-static hipError_t launch_one(const GemmProblem &p, hipStream_t stream) {
+static hipError_t launch_one(const GemmProblem &p, const StreamKPlan &sk, const TileWorkspace &ws,
+                             hipStream_t stream) {
     if (p.kbytes < BKB)   // no full K tile: the ring kernel needs at least one
         return launch_generic<P>(p, stream);
     int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-    dim3 grid(tiles_m * tiles_n), block(64 * WGM * WGN);
-    hipLaunchKernelGGL((gemm_tile_kernel<P, BM, BN, BKB, WGM, WGN, NS>), grid, block, 0, stream, p,
-                       tiles_m, tiles_n);
+    dim3 block(64 * WGM * WGN);
+    if (sk.grid > 0) {
+        // the plan was made for this tile shape and workspace
+        if (sk.tiles_dp + sk.sk_tiles != tiles_m * tiles_n || sk.sk_tiles > ws.flag_count ||
+            2 * (int64_t)sk.grid * BM * BN * 4 > ws.partial_bytes || sk.iters < sk.grid ||
+            sk.iters != (int64_t)sk.sk_tiles * ((p.kbytes + BKB - 1) / BKB))
+            return hipErrorInvalidValue;
+        StreamKArgs a;
+        a.tiles_dp = sk.tiles_dp;
+        a.iters = sk.iters;
+        a.partial = ws.partial;
+        a.partial_bytes = (int)(2 * (int64_t)sk.grid * BM * BN * 4);
+        a.flags = ws.flags;
+        hipLaunchKernelGGL((gemm_tile_sk_kernel<P, BM, BN, BKB, WGM, WGN, NS>), dim3(sk.grid), block,
+                           0, stream, p, tiles_m, tiles_n, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((gemm_tile_kernel<P, BM, BN, BKB, WGM, WGN, NS>), dim3(tiles_m * tiles_n),
+                       block, 0, stream, p, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -539,27 +772,29 @@ static hipError_t launch_generic(const GemmProblem &p, hipStream_t stream) {
 }
 
 template <int P>
-static hipError_t launch_prec(int cfg, const GemmProblem &p, bool aligned, hipStream_t stream) {
+static hipError_t launch_prec(int cfg, const GemmProblem &p, const StreamKPlan &sk,
+                              const TileWorkspace &ws, bool aligned, hipStream_t stream) {
     if (!aligned)   // byte-gather loads, one shape
         return launch_generic<P>(p, stream);
     switch (cfg) {
-    case CFG_256x256: return launch_one<P, 256, 256, 64, 2, 2, 4>(p, stream);
-    case CFG_128x128: return launch_one<P, 128, 128, 64, 2, 2, 4>(p, stream);
-    case CFG_64x64: return launch_one<P, 64, 64, 128, 2, 2, 3>(p, stream);
-    case CFG_256x128: return launch_one<P, 256, 128, 128, 2, 2, 3>(p, stream);
-    case CFG_256x256_BK128: return launch_one<P, 256, 256, 128, 2, 2, 2>(p, stream);
-    case CFG_128x256: return launch_one<P, 128, 256, 128, 2, 2, 3>(p, stream);
-    case CFG_128x128_BK128: return launch_one<P, 128, 128, 128, 2, 2, 4>(p, stream);
-    case CFG_256x256_W8: return launch_one<P, 256, 256, 128, 4, 2, 2>(p, stream);
-    case CFG_256x256_W8_BK64: return launch_one<P, 256, 256, 64, 4, 2, 4>(p, stream);
-    case CFG_256x128_2B: return launch_one<P, 256, 128, 64, 2, 2, 3>(p, stream);
-    case CFG_128x128_2B: return launch_one<P, 128, 128, 128, 2, 2, 2>(p, stream);
-    case CFG_128x256_2B: return launch_one<P, 128, 256, 64, 2, 2, 3>(p, stream);
+    case CFG_256x256: return launch_one<P, 256, 256, 64, 2, 2, 4>(p, sk, ws, stream);
+    case CFG_128x128: return launch_one<P, 128, 128, 64, 2, 2, 4>(p, sk, ws, stream);
+    case CFG_64x64: return launch_one<P, 64, 64, 128, 2, 2, 3>(p, sk, ws, stream);
+    case CFG_256x128: return launch_one<P, 256, 128, 128, 2, 2, 3>(p, sk, ws, stream);
+    case CFG_256x256_BK128: return launch_one<P, 256, 256, 128, 2, 2, 2>(p, sk, ws, stream);
+    case CFG_128x256: return launch_one<P, 128, 256, 128, 2, 2, 3>(p, sk, ws, stream);
+    case CFG_128x128_BK128: return launch_one<P, 128, 128, 128, 2, 2, 4>(p, sk, ws, stream);
+    case CFG_256x256_W8: return launch_one<P, 256, 256, 128, 4, 2, 2>(p, sk, ws, stream);
+    case CFG_256x256_W8_BK64: return launch_one<P, 256, 256, 64, 4, 2, 4>(p, sk, ws, stream);
+    case CFG_256x128_2B: return launch_one<P, 256, 128, 64, 2, 2, 3>(p, sk, ws, stream);
+    case CFG_128x128_2B: return launch_one<P, 128, 128, 128, 2, 2, 2>(p, sk, ws, stream);
+    case CFG_128x256_2B: return launch_one<P, 128, 256, 64, 2, 2, 3>(p, sk, ws, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_gemm(int prec, int cfg, const GemmProblem &p, hipStream_t stream) {
+hipError_t launch_gemm(int prec, int cfg, const GemmProblem &p, const StreamKPlan &sk,
+                       const TileWorkspace &ws, hipStream_t stream) {
     // The fast kernel needs 16-byte aligned rows and 32-bit offsets within the
     // 256 rows of a tile.
     const int64_t kRowLimit = (int64_t)1 << 23;
@@ -567,10 +802,10 @@ hipError_t launch_gemm(int prec, int cfg, const GemmProblem &p, hipStream_t stre
                          (reinterpret_cast<uintptr_t>(p.B) % 16 == 0) && p.lda_b % 16 == 0 &&
                          p.ldb_b % 16 == 0 && p.lda_b < kRowLimit && p.ldb_b < kRowLimit;
     switch (prec) {
-    case PREC_F16: return launch_prec<PREC_F16>(cfg, p, aligned, stream);
-    case PREC_I8: return launch_prec<PREC_I8>(cfg, p, aligned, stream);
-    case PREC_I4: return launch_prec<PREC_I4>(cfg, p, aligned, stream);
-    case PREC_W4A4: return launch_prec<PREC_W4A4>(cfg, p, aligned, stream);
+    case PREC_F16: return launch_prec<PREC_F16>(cfg, p, sk, ws, aligned, stream);
+    case PREC_I8: return launch_prec<PREC_I8>(cfg, p, sk, ws, aligned, stream);
+    case PREC_I4: return launch_prec<PREC_I4>(cfg, p, sk, ws, aligned, stream);
+    case PREC_W4A4: return launch_prec<PREC_W4A4>(cfg, p, sk, ws, aligned, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -45,7 +45,44 @@ enum TileCfg {
 
 const char *tile_cfg_name(int cfg);
 int choose_tile_cfg(int prec, int64_t M, int64_t N, int64_t kbytes, int cu_count);
-hipError_t launch_gemm(int prec, int cfg, const GemmProblem &p, hipStream_t stream);
+
+// Device memory of a handle that stream-K launches use: partial tiles and one
+// arrival counter per split tile (all counters zero between launches).
+struct TileWorkspace {
+    void *partial;
+    int64_t partial_bytes;
+    int *flags;
+    int flag_count;
+};
+
+// Arguments of the stream-K kernel: tiles [0, tiles_dp) run whole,
+// round-robin over the grid; the K iterations of the other tiles (iters in
+// total) are split evenly over the grid. partial holds 2 tiles of BM x BN
+// 4-byte accumulators per workgroup.
+struct StreamKArgs {
+    int tiles_dp;
+    int64_t iters;
+    void *partial;
+    int partial_bytes;
+    int *flags;
+};
+
+// grid == 0: data-parallel launch (one workgroup per tile).
+struct StreamKPlan {
+    int grid;
+    int tiles_dp;
+    int sk_tiles;
+    int64_t iters;
+};
+
+// Stream-K policy: MODE_AUTO decides by the fill of the last wave of tiles,
+// MODE_OFF never splits, MODE_ON splits whenever the tiles do not fill whole
+// waves of the grid (the ablation override).
+enum StreamKMode { SK_MODE_AUTO = -1, SK_MODE_OFF = 0, SK_MODE_ON = 1 };
+StreamKPlan plan_stream_k(int cfg, int64_t M, int64_t N, int64_t kbytes, int cu_count,
+                          int64_t partial_bytes, int flag_count, int mode);
+hipError_t launch_gemm(int prec, int cfg, const GemmProblem &p, const StreamKPlan &sk,
+                       const TileWorkspace &ws, hipStream_t stream);
 
 // Weight-only INT4 GEMM Y = X * dequant(Wq)^T.
 struct W4A16Problem {

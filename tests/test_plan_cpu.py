@@ -28,7 +28,8 @@ def test_tile_config_at_the_workload_sizes(mp, prec):
     and 1024, 128x128 with a 4-stage ring at 2048, 256x256 from 4096 on."""
     want = {512: 2, 1024: 2, 2048: 6, 4096: 4, 8192: 4}
     for n, cfg in want.items():
-        assert mp.mpgemm_plan_gemm(prec, n, n, n, 256) == (OK, cfg), n
+        # whole waves of tiles (or a grid below one wave): data-parallel
+        assert mp.mpgemm_plan_gemm(prec, n, n, n, 256) == (OK, cfg, 0, 0), n
 
 
 def test_tile_config_fills_the_compute_units(mp):
@@ -38,12 +39,107 @@ def test_tile_config_fills_the_compute_units(mp):
     rng = np.random.default_rng(0)
     for _ in range(500):
         M, N, K = (int(v) for v in rng.integers(1, 20000, 3))
-        st, cfg = mp.mpgemm_plan_gemm(1, M, N, K, 256)
+        st, cfg, _, _ = mp.mpgemm_plan_gemm(1, M, N, K, 256)
         assert st == OK and cfg in (2, 3, 4, 6)
         if cfg != 2:
             bm = tiles[cfg]
             bn = 128 if cfg == 3 else bm
             assert -(-M // bm) * -(-N // bn) >= 128
+
+
+# tile configurations: (BM, BN, K bytes per stage, workgroups per compute unit)
+TILE = {0: (256, 256, 64, 1), 1: (128, 128, 64, 2), 2: (64, 64, 128, 3), 3: (256, 128, 128, 1),
+        4: (256, 256, 128, 1), 5: (128, 256, 128, 1), 6: (128, 128, 128, 1)}
+KBYTES = {0: lambda K: 2 * K, 1: lambda K: K, 2: lambda K: K // 2, 3: lambda K: K // 2}
+WORKSPACE_BYTES = 128 << 20
+
+
+def sk_partition(tiles_sk, KT, grid):
+    """Segments (workgroup, tile, first entry, end entry, slot) of the stream-K
+    part, with the ranges and slot rule of the kernel: workgroup w runs
+    iterations [w I / G, (w+1) I / G); a partial tile goes to slot 0 when the
+    workgroup's range starts inside it, else slot 1."""
+    I = tiles_sk * KT
+    segs = []
+    for w in range(grid):
+        beg, end = I * w // grid, I * (w + 1) // grid
+        it = beg
+        while it < end:
+            t, e0 = divmod(it, KT)
+            e1 = min(KT, e0 + end - it)
+            slot = 0 if beg >= t * KT else 1
+            segs.append((w, t, e0, e1, slot))
+            it += e1 - e0
+    return segs
+
+
+def owner(x, I, grid):
+    return ((x + 1) * grid - 1) // I
+
+
+def test_stream_k_partition_invariants():
+    """Every K iteration of every split tile is run exactly once, a workgroup
+    has at most two partial tiles and they use distinct workspace slots, and
+    the contributors of a tile are the contiguous workgroups the kernel's
+    owner formula names."""
+    rng = np.random.default_rng(2)
+    cases = [(1, 2, 1), (3, 7, 5), (16, 10, 160), (289, 64, 256), (300, 33, 256)]
+    cases += [(int(rng.integers(1, 600)), int(rng.integers(2, 80)), 0) for _ in range(300)]
+    for tiles_sk, KT, grid in cases:
+        I = tiles_sk * KT
+        if grid == 0:
+            grid = int(rng.integers(1, 600))
+        grid = min(grid, I)
+        segs = sk_partition(tiles_sk, KT, grid)
+        cover = np.zeros(I, np.int64)
+        used = set()
+        for w, t, e0, e1, slot in segs:
+            assert 0 <= e0 < e1 <= KT
+            cover[t * KT + e0:t * KT + e1] += 1
+            if not (e0 == 0 and e1 == KT):
+                assert (w, slot) not in used
+                used.add((w, slot))
+        assert (cover == 1).all()
+        by_tile = {}
+        for w, t, e0, e1, slot in segs:
+            by_tile.setdefault(t, []).append(w)
+        for t, ws in by_tile.items():
+            lo, hi = owner(t * KT, I, grid), owner(t * KT + KT - 1, I, grid)
+            assert ws == list(range(lo, hi + 1)), (tiles_sk, KT, grid, t)
+
+
+def test_stream_k_plan(mp):
+    """Auto policy: a stream-K grid only for a short last wave (at most half a
+    wave of tiles) after at least one full wave; the last full wave joins the
+    split part; the partial tiles fit the handle's workspace."""
+    rng = np.random.default_rng(3)
+    seen = 0
+    for _ in range(2000):
+        prec = int(rng.integers(0, 4))
+        M, N = (int(v) for v in rng.integers(1, 12000, 2))
+        K = int(rng.integers(1, 9000)) * 2
+        st, cfg, grid, tdp = mp.mpgemm_plan_gemm(prec, M, N, K, 256)
+        assert st == OK
+        BM, BN, BKB, per_cu = TILE[cfg]
+        T = -(-M // BM) * -(-N // BN)
+        G = 256 * per_cu
+        KT = -(-KBYTES[prec](K) // BKB)
+        if grid == 0:
+            assert tdp == 0
+            assert T % G == 0 or T < G or 2 * (T % G) > G or KT < 2 or KBYTES[prec](K) < BKB
+            continue
+        seen += 1
+        full, rem = divmod(T, G)
+        assert full >= 1 and 0 < 2 * rem <= G
+        assert tdp == (full - 1) * G and grid == G
+        assert 2 * grid * BM * BN * 4 <= WORKSPACE_BYTES
+    assert seen > 20
+
+
+def test_stream_k_at_a_ragged_size(mp):
+    """N = 6144 FP16: 576 tiles of 256 x 256 are 2.25 waves on 256 compute
+    units; the plan runs one wave whole and splits the other 320 tiles."""
+    assert mp.mpgemm_plan_gemm(0, 6144, 6144, 6144, 256) == (OK, 4, 256, 256)
 
 
 def test_plan_gemm_arguments(mp):
