@@ -424,6 +424,136 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p
     RT::epilogue(p, smem, row0, col0, tid, lane, wave, acc);
 }
 
+// Ping-pong kernel for the 256 x 256 tile (data-parallel, K a multiple of
+// the 128-byte stage, at least two stages). Eight wavefronts, two per SIMD,
+// in two groups of four (wavefronts q and q + 4 share SIMD q) that run the
+// same loop one phase apart. A phase ends at a workgroup barrier; in each
+// phase one group issues the MFMAs of two k-steps from fragments that are
+// already in its registers, while the other group reads the fragments of its
+// next two k-steps from LDS and issues its share of the direct-to-LDS loads.
+// A wavefront's fragment reads are then covered by its SIMD partner's MFMAs
+// instead of its own. The price is 1.5x the fragment bytes per MFMA (128 x 64
+// wavefront tiles instead of 128 x 128): four wavefronts reading 12 KiB each
+// per phase need about as long as the phase's MFMAs, so on MI355X the memory
+// half, not the matrix unit, sets the pace. Measured slower than the
+// four-wavefront ring kernel except for INT8 at 4096; kept as an ablation
+// configuration (the override index CFG_256x256_PP).
+//
+// Wavefront (g, q): rows [128 (q / 2), +128), columns [128 (q % 2) + 64 g,
+// +64) of the tile. Stage e (entry e of K) lives in LDS stage e % 2 and is
+// read in the group's phase pairs 2e and 2e + 1. Entry e + 1 (e >= 1) is
+// loaded during pair 2e into the stage that entry e - 1 used (free: the last
+// read of it ended before the barrier that opens pair 2e), and every
+// wavefront waits for its own loads at the end of the memory half of pair
+// 2e + 1, so the barrier that follows publishes the entry to both groups
+// before pair 2e + 2.
+template <int P>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, int tiles_m, int tiles_n) {
+    constexpr int BM = 256, BN = 256, BKB = 128, NS = 2, NT = 512;
+    constexpr int CPR = BKB / 16;                      // 16-byte chunks per LDS row
+    constexpr int RS = NT / CPR;                       // rows per load round
+    constexpr int A_PER_T = BM / RS, B_PER_T = BN / RS;
+    constexpr int NL = A_PER_T + B_PER_T;              // loads per thread per stage
+    constexpr int STAGE = (BM + BN) * BKB;
+    constexpr int PS = 2;                              // k-steps per phase
+    constexpr int PAIRS = (CPR / 2) / PS;              // phases per stage and group
+    constexpr int TM = 4, TN = 2;                      // 128 x 64 per wavefront
+    static_assert(PAIRS == 2, "the load schedule assumes two phases per stage");
+    typedef typename AccOf<P>::type acc_t;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, q = wave & 3;
+    const int wm0 = (q >> 1) * 128, wn0 = (q & 1) * 128 + grp * 64;
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int row0 = tm * BM, col0 = tn * BN;
+    const int KT = (int)(p.kbytes / BKB);
+
+    // direct-to-LDS addressing as in RingTile: thread rows r0 + i * RS, the
+    // global chunk that the swizzle puts in the thread's LDS slot
+    const int r0 = tid / CPR;
+    const int cg = (tid % CPR) ^ swz<CPR>(r0);
+    const uint8_t *Ab = p.A + (int64_t)row0 * p.lda_b;
+    const uint8_t *Bb = p.B + (int64_t)col0 * p.ldb_b;
+    const int a_rows = p.M - row0, b_rows = p.N - col0;
+    uint32_t off[NL];
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+        int r = r0 + i * RS;
+        r = r < a_rows ? r : a_rows - 1;   // clamped rows feed outputs never stored
+        off[i] = (uint32_t)r * (uint32_t)p.lda_b + cg * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) {
+        int r = r0 + i * RS;
+        r = r < b_rows ? r : b_rows - 1;
+        off[A_PER_T + i] = (uint32_t)r * (uint32_t)p.ldb_b + cg * 16;
+    }
+    const int wrow = wave * (64 / CPR);
+    auto dma_entry = [&](int kt) {
+        const uint8_t *a = Ab + (int64_t)kt * BKB;
+        const uint8_t *b = Bb + (int64_t)kt * BKB;
+        uint8_t *S = smem + (kt % NS) * STAGE + wrow * BKB;
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i)
+            dma16(a + off[i], S + i * RS * BKB);
+#pragma unroll
+        for (int i = 0; i < B_PER_T; ++i)
+            dma16(b + off[A_PER_T + i], S + BM * BKB + i * RS * BKB);
+    };
+
+    acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = acc_t{};
+    i32x4 fa[PS][TM], fb[PS][TN];
+
+    dma_entry(0);
+    dma_entry(1);
+    wait_vm_lds<0>();
+    lds_barrier();
+    if (grp == 1)
+        lds_barrier();   // group 1 runs one phase behind group 0
+
+    const int NPAIR = KT * PAIRS;
+    for (int j = 0; j < NPAIR; ++j) {
+        const int e = j / PAIRS, h = j % PAIRS;
+        const uint8_t *S = smem + (e % NS) * STAGE;
+        // memory half: fragments of k-steps h PS .. h PS + PS - 1 of entry e
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < PS; ++s)
+            read_frags<BM, BKB, TM, TN>(S, h * PS + s, wm0, wn0, lane, fa[s], fb[s]);
+        if (h == 0 && e >= 1 && e + 1 < KT)
+            dma_entry(e + 1);
+        if (h == PAIRS - 1)
+            wait_vm_lds<0>();    // this wavefront's loads of entry e + 1 have landed
+        else
+            wait_vm_lds<63>();   // fragment reads only
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        // compute half
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s = 0; s < PS; ++s)
+            mfma_step<P, TM, TN>(fa[s], fb[s], acc);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+    }
+    if (grp == 0)
+        lds_barrier();   // same barrier count in both groups
+
+    store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc);
+}
+
 // Stream-K partial accumulators: 16-byte loads and stores that are coherent
 // across the XCDs' L2 caches (sc1: written through, read past a stale line),
 // so that no cache-wide write-back or invalidation is needed.
@@ -670,6 +800,7 @@ static const CfgShape kCfg[CFG_COUNT] = {
     {256, 128, 64, 2, "256x128_bk64_ring3_2blk"},
     {128, 128, 128, 2, "128x128_bk128_ring2_2blk"},
     {128, 256, 64, 2, "128x256_bk64_ring3_2blk"},
+    {256, 256, 128, 1, "256x256_bk128_pingpong"},
 };
 
 const char *tile_cfg_name(int cfg) {
@@ -763,6 +894,14 @@ static hipError_t launch_one(const GemmProblem &p, const StreamKPlan &sk, const 
 }
 
 template <int P>
+static hipError_t launch_pp(const GemmProblem &p, hipStream_t stream) {
+    const int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
+    hipLaunchKernelGGL((gemm_pp_kernel<P>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, p, tiles_m,
+                       tiles_n);
+    return hipGetLastError();
+}
+
+template <int P>
 static hipError_t launch_generic(const GemmProblem &p, hipStream_t stream) {
     constexpr int BM = 128, BN = 128;
     int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
@@ -789,6 +928,14 @@ static hipError_t launch_prec(int cfg, const GemmProblem &p, const StreamKPlan &
     case CFG_256x128_2B: return launch_one<P, 256, 128, 64, 2, 2, 3>(p, sk, ws, stream);
     case CFG_128x128_2B: return launch_one<P, 128, 128, 128, 2, 2, 2>(p, sk, ws, stream);
     case CFG_128x256_2B: return launch_one<P, 128, 256, 64, 2, 2, 3>(p, sk, ws, stream);
+    case CFG_256x256_PP:
+        if constexpr (P != PREC_W4A4) {
+            if (sk.grid == 0 && p.kbytes % 128 == 0 && p.kbytes >= 256)
+                return launch_pp<P>(p, stream);
+        }
+        // stream-K, a partial K tile or the W4A4 epilogue: the ring kernel of
+        // the same tile shape
+        return launch_one<P, 256, 256, 128, 2, 2, 2>(p, sk, ws, stream);
     default: return hipErrorInvalidValue;
     }
 }

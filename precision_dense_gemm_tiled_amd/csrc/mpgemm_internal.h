@@ -40,6 +40,7 @@ enum TileCfg {
     CFG_256x128_2B = 9,     // 4 waves of 128x64, BK = 64 B, 3 stages: 72 KiB, two blocks per CU
     CFG_128x128_2B = 10,    // 4 waves of 64x64, BK = 128 B, 2 stages: 64 KiB, two blocks per CU
     CFG_128x256_2B = 11,    // 4 waves of 64x128, BK = 64 B, 3 stages: 72 KiB, two blocks per CU
+    CFG_256x256_PP = 12,    // 8 waves of 128x64 in two ping-pong groups, BK = 128 B, 2 stages
     CFG_COUNT
 };
 

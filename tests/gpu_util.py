@@ -3,6 +3,11 @@ import math
 
 import numpy as np
 
+# Tile configurations of the GEMM kernels (indices of the MPGEMM_TILE_CFG
+# override): 0-11 the ring kernel's shapes, 12 the 256 x 256 ping-pong kernel.
+N_TILE_CFGS = 13
+PINGPONG_CFG = 12
+
 
 def require_gpu():
     import torch

@@ -12,8 +12,8 @@ import pytest
 import oracle
 import precision_dense_gemm_tiled_amd as mp
 from precision_dense_gemm_tiled_amd import inputs
-from tests.gpu_util import (dev, f16_tol, freivalds_int, host, pack_i4, require_gpu,
-                            sample_rows, unpack_i4, w4a16_tol)
+from tests.gpu_util import (N_TILE_CFGS, PINGPONG_CFG, dev, f16_tol, freivalds_int, host, pack_i4,
+                            require_gpu, sample_rows, unpack_i4, w4a16_tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +69,7 @@ def test_every_tile_config(prec, monkeypatch):
     M, N, K = 300, 520, 200
     A, B = inputs.gemm_problem(prec, M, N, K, seed=77)
     ref = _ref(prec, A, B, K)
-    for cfg in range(12):
+    for cfg in range(N_TILE_CFGS):
         monkeypatch.setenv("MPGEMM_TILE_CFG", str(cfg))
         with mp.Handle() as h:
             a, b = dev(A), dev(B)
@@ -80,6 +80,34 @@ def test_every_tile_config(prec, monkeypatch):
             else:
                 got = host(mp.gemm_f16(a, b, handle=h.value))
         _compare(prec, got, ref, K, f"{prec} cfg {cfg}")
+
+
+# (M, N, K bytes per row): the ping-pong kernel needs K in whole 128-byte
+# stages, at least two; ragged M and N tiles, a single output, one tile, a
+# grid of several tiles with a longer K.
+PINGPONG_SHAPES = [(300, 520, 256), (513, 260, 1024), (1, 1, 256), (256, 256, 384), (700, 1000, 2048)]
+
+
+@pytest.mark.parametrize("prec", ["i8", "i4", "f16"])
+@pytest.mark.parametrize("M,N,kb", PINGPONG_SHAPES)
+def test_pingpong_config(prec, M, N, kb, monkeypatch):
+    """The 256 x 256 ping-pong kernel (forced) against the oracle, and a
+    second call on the same inputs bit-identical to the first."""
+    K = {"i8": kb, "f16": kb // 2, "i4": 2 * kb}[prec]
+    A, B = inputs.gemm_problem(prec, M, N, K, seed=1000 + M + N + kb)
+    monkeypatch.setenv("MPGEMM_TILE_CFG", str(PINGPONG_CFG))
+    with mp.Handle() as h:
+        a, b = dev(A), dev(B)
+        runs = []
+        for _ in range(2):
+            if prec == "i8":
+                runs.append(host(mp.gemm_i8(a, b, handle=h.value)))
+            elif prec == "i4":
+                runs.append(host(mp.gemm_i4(a, b, K, handle=h.value)))
+            else:
+                runs.append(host(mp.gemm_f16(a, b, handle=h.value)))
+    _compare(prec, runs[0], _ref(prec, A, B, K), K, f"{prec} ping-pong {M}x{N}x{K}")
+    assert np.array_equal(runs[0].view(np.uint32), runs[1].view(np.uint32)), "repeat differs"
 
 
 def test_i4_equals_i8_of_unpacked_on_gpu():
@@ -363,7 +391,7 @@ def test_w4a4_against_oracle(M, N, K, with_bias):
 def test_w4a4_every_tile_config(monkeypatch):
     M, N, K = 300, 520, 200
     A, B, sx, sw, b = inputs.w4a4_problem(M, N, K, seed=78)
-    for cfg in range(12):
+    for cfg in range(N_TILE_CFGS):
         monkeypatch.setenv("MPGEMM_TILE_CFG", str(cfg))
         with mp.Handle() as h:
             got = host(mp.gemm_w4a4(dev(A), dev(B), K, dev(sx), dev(sw), dev(b), handle=h.value))

@@ -13,7 +13,7 @@ import pytest
 import oracle
 import precision_dense_gemm_tiled_amd as mp
 from precision_dense_gemm_tiled_amd import inputs
-from tests.gpu_util import dev, f16_tol, freivalds_int, host, require_gpu, sample_rows
+from tests.gpu_util import dev, f16_tol, freivalds_int, host, require_gpu, sample_rows, N_TILE_CFGS
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +62,7 @@ def test_every_tile_config_forced(prec, monkeypatch):
     A, B = inputs.gemm_problem(prec, M, N, K, seed=91)
     ref = _ref(prec, A, B, K)
     monkeypatch.setenv("MPGEMM_STREAMK", "1")
-    for cfg in range(12):
+    for cfg in range(N_TILE_CFGS):
         monkeypatch.setenv("MPGEMM_TILE_CFG", str(cfg))
         with mp.Handle() as h:
             got = _run(prec, A, B, K, h.value)
@@ -149,7 +149,7 @@ def test_w4a4_every_tile_config_forced(monkeypatch):
     mag = c_abs * np.abs(sx.astype(np.float64))[:, None] * np.abs(sw.astype(np.float64))[None, :]
     tol = 2.0 ** -11 * np.abs(y) + 3 * 2.0 ** -24 * (mag + np.abs(b.astype(np.float64))[None, :]) + 2.0 ** -24
     monkeypatch.setenv("MPGEMM_STREAMK", "1")
-    for cfg in range(12):
+    for cfg in range(N_TILE_CFGS):
         monkeypatch.setenv("MPGEMM_TILE_CFG", str(cfg))
         with mp.Handle() as h:
             got = host(mp.gemm_w4a4(dev(A), dev(B), K, dev(sx), dev(sw), dev(b), handle=h.value))
