@@ -175,6 +175,46 @@ def test_strided_operands_and_output():
         assert np.all(whole[:, N:] == -1), "wrote past N"
 
 
+# Output layouts of the epilogue: (row stride, first column) of C inside a
+# larger buffer, with padding on both sides that must stay untouched: strides
+# that are multiples of 4 and 16-byte aligned rows, a first column at an odd
+# element, an odd stride; N = 90 is not a multiple of the 32-column blocks.
+OUTPUT_LAYOUTS = [(96, 0), (96, 1), (93, 0), (100, 4)]
+
+
+@pytest.mark.parametrize("prec", ["i8", "i4", "f16"])
+@pytest.mark.parametrize("ldc,c0", OUTPUT_LAYOUTS)
+def test_output_layouts(prec, ldc, c0):
+    import torch
+    M, N, K = 70, 90, 256
+    A, B = inputs.gemm_problem(prec, M, N, K, seed=ldc + c0)
+    cdt = torch.float32 if prec == "f16" else torch.int32
+    cbig = torch.full((M, ldc), -1, dtype=cdt, device="cuda")
+    c = cbig[:, c0:c0 + N]
+    a, b = dev(A), dev(B)
+    if prec == "i8":
+        mp.gemm_i8(a, b, out=c)
+    elif prec == "i4":
+        mp.gemm_i4(a, b, K, out=c)
+    else:
+        mp.gemm_f16(a, b, out=c)
+    whole = host(cbig)
+    _compare(prec, whole[:, c0:c0 + N], _ref(prec, A, B, K), K, f"{prec} ldc {ldc} col {c0}")
+    assert np.all(whole[:, :c0] == -1) and np.all(whole[:, c0 + N:] == -1), "wrote outside C"
+
+
+@pytest.mark.parametrize("ldc,c0", OUTPUT_LAYOUTS)
+def test_w4a4_output_layouts(ldc, c0):
+    import torch
+    M, N, K = 70, 90, 256
+    A, B, sx, sw, b = inputs.w4a4_problem(M, N, K, seed=ldc + c0)
+    ybig = torch.full((M, ldc), -1.0, dtype=torch.float16, device="cuda")
+    mp.gemm_w4a4(dev(A), dev(B), K, dev(sx), dev(sw), dev(b), out=ybig[:, c0:c0 + N])
+    whole = host(ybig)
+    _w4a4_check(A, B, K, sx, sw, b, whole[:, c0:c0 + N], f"w4a4 ldc {ldc} col {c0}")
+    assert np.all(whole[:, :c0] == -1) and np.all(whole[:, c0 + N:] == -1), "wrote outside Y"
+
+
 @pytest.mark.parametrize("prec", ["i8", "i4", "f16"])
 def test_unaligned_operands_byte_gather_path(prec):
     """Operands whose rows are not 16-byte aligned (odd strides, offset base)
