@@ -233,7 +233,24 @@ __device__ __forceinline__ void stage_factors(const GemmProblem &p, int row0, in
 // (loaded through registers with K masking); entry e >= NPRE is full K tile
 // e - NPRE. The caller guarantees 0 <= e0 < e1 <= KT and that the ring is
 // free (no wavefront still reads it). On return every load has landed.
-template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS>
+//
+// VAR selects one change at a time for the ablation configurations (the L4
+// study's pipeline ablations: separate loaders for the two operands, the
+// load cache policy, and on gfx950 also the staging path): 0 the kernel as
+// described; 1 split loaders (the first half of the wavefronts loads every
+// A row of the stage, the second half every B row); 2 the tile loads marked
+// non-temporal (nt); 3 the tile loads at device scope (sc1); 4 tile loads
+// staged through VGPRs (global_load_dwordx4, then ds_write_b128 into the free
+// stage before the barrier that publishes it) instead of direct-to-LDS.
+enum { VAR_BASE = 0, VAR_SPLIT = 1, VAR_NT = 2, VAR_SC1 = 3, VAR_VGPR = 4 };
+
+template <int AUX>
+__device__ __forceinline__ void dma16_cp(const void *g, void *lds) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds, 16, 0, AUX);
+}
+
+template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS, int VAR = VAR_BASE>
 struct RingTile {
     static constexpr int NT = 64 * WGM * WGN;
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -242,6 +259,12 @@ struct RingTile {
     static constexpr int RS = NT / CPR;
     static constexpr int A_PER_T = BM / RS, B_PER_T = BN / RS;
     static constexpr int NL = A_PER_T + B_PER_T;   // direct-to-LDS loads per thread per tile
+    static constexpr bool SPLIT = VAR == VAR_SPLIT;
+    static constexpr bool VSTAGE = VAR == VAR_VGPR;
+    static constexpr int CPOL = VAR == VAR_NT ? 2 : (VAR == VAR_SC1 ? 16 : 0);
+    static constexpr int RSL = SPLIT ? RS / 2 : RS;   // rows per load round of one loader
+    static constexpr int HW = NT / 128;                // wavefronts per operand when split
+    static_assert(!SPLIT || (BM == BN && (NT / 2) % 64 == 0 && RSL % 16 == 0), "split loaders");
     static constexpr int STAGE = (BM + BN) * BKB;
     static constexpr int STEPS = CPR / 2;
     static constexpr int LDS_BYTES = NS * STAGE;
@@ -264,26 +287,29 @@ struct RingTile {
         const bool tail = (kbytes % BKB) != 0;  // plus one partial tile
         const int NPRE = tail ? 1 : 0;
 
-        const int r0 = tid / CPR;
+        // Load i of this thread: operand A or B, row r0 + step. With split
+        // loaders a wavefront loads one operand only (wave-uniform choice).
+        const bool a_wave = !SPLIT || wave < HW;
+        const int r0 = (SPLIT ? tid % (NT / 2) : tid) / CPR;
         const int cg = (tid % CPR) ^ swz<CPR>(r0);   // global chunk of this lane's slot
+        auto ld_is_a = [&](int i) { return SPLIT ? a_wave : i < A_PER_T; };
+        auto ld_step = [&](int i) { return SPLIT ? i * RSL : (i < A_PER_T ? i : i - A_PER_T) * RS; };
         const uint8_t *Ab = p.A + (int64_t)row0 * p.lda_b;
         const uint8_t *Bb = p.B + (int64_t)col0 * p.ldb_b;
         const int a_rows = p.M - row0, b_rows = p.N - col0;   // >= 1
         uint32_t off[NL];
 #pragma unroll
-        for (int i = 0; i < A_PER_T; ++i) {
-            int r = r0 + i * RS;
-            r = r < a_rows ? r : a_rows - 1;   // clamped rows feed outputs never stored
-            off[i] = (uint32_t)r * (uint32_t)p.lda_b + cg * 16;
-        }
-#pragma unroll
-        for (int i = 0; i < B_PER_T; ++i) {
-            int r = r0 + i * RS;
-            r = r < b_rows ? r : b_rows - 1;
-            off[A_PER_T + i] = (uint32_t)r * (uint32_t)p.ldb_b + cg * 16;
+        for (int i = 0; i < NL; ++i) {
+            const bool isa = ld_is_a(i);
+            const int rows = isa ? a_rows : b_rows;
+            int r = r0 + ld_step(i);
+            r = r < rows ? r : rows - 1;   // clamped rows feed outputs never stored
+            off[i] = (uint32_t)r * (uint32_t)(isa ? p.lda_b : p.ldb_b) + cg * 16;
         }
         // wave-uniform LDS base of this wavefront's DMA rows within a stage
-        const int wrow = wave * (64 / CPR);
+        const int wrow = (SPLIT ? wave % HW : wave) * (64 / CPR);
+        auto ld_dst = [&](int i) { return (ld_is_a(i) ? 0 : BM * BKB) + (wrow + ld_step(i)) * BKB; };
+        i32x4 R[VSTAGE ? NL : 1];   // staging registers of the VGPR-staged variant
 
         // Every call issues exactly NL loads (entries past the last full tile
         // re-read it into a stage that is free), so a fixed vmcnt tells which
@@ -294,28 +320,34 @@ struct RingTile {
             kt = kt < KF - 1 ? kt : KF - 1;
             const uint8_t *a = Ab + (int64_t)kt * BKB;
             const uint8_t *b = Bb + (int64_t)kt * BKB;
-            uint8_t *S = smem + (e % NS) * STAGE + wrow * BKB;
+            uint8_t *S = smem + (e % NS) * STAGE;
 #pragma unroll
-            for (int i = 0; i < A_PER_T; ++i)
-                dma16(a + off[i], S + i * RS * BKB);
+            for (int i = 0; i < NL; ++i) {
+                const uint8_t *src = (ld_is_a(i) ? a : b) + off[i];
+                if constexpr (VSTAGE)
+                    R[i] = *reinterpret_cast<const i32x4 *>(src);
+                else
+                    dma16_cp<CPOL>(src, S + ld_dst(i));
+            }
+        };
+        // VGPR-staged variant: the registers of entry e -> its stage
+        auto stage_regs = [&](int e) {
+            if constexpr (VSTAGE) {
+                uint8_t *S = smem + (e % NS) * STAGE + lane * 16;
 #pragma unroll
-            for (int i = 0; i < B_PER_T; ++i)
-                dma16(b + off[A_PER_T + i], S + BM * BKB + i * RS * BKB);
+                for (int i = 0; i < NL; ++i)
+                    *reinterpret_cast<i32x4 *>(S + ld_dst(i)) = R[i];
+            }
         };
         // partial tile kt -> stage 0 through registers, bytes past K cleared
         auto reg_tail = [&](int kt) {
             const int64_t k0 = (int64_t)kt * BKB + cg * 16;
-            uint8_t *S = smem + r0 * BKB + ((tid % CPR) * 16);
 #pragma unroll
-            for (int i = 0; i < A_PER_T; ++i) {
-                const i32x4 v = load_chunk_masked(Ab + (off[i] - cg * 16), k0, kbytes, r0 + i * RS < a_rows);
-                *reinterpret_cast<i32x4 *>(S + i * RS * BKB) = v;
-            }
-#pragma unroll
-            for (int i = 0; i < B_PER_T; ++i) {
-                const i32x4 v = load_chunk_masked(Bb + (off[A_PER_T + i] - cg * 16), k0, kbytes,
-                                                  r0 + i * RS < b_rows);
-                *reinterpret_cast<i32x4 *>(S + BM * BKB + i * RS * BKB) = v;
+            for (int i = 0; i < NL; ++i) {
+                const bool isa = ld_is_a(i);
+                const i32x4 v = load_chunk_masked((isa ? Ab : Bb) + (off[i] - cg * 16), k0, kbytes,
+                                                  r0 + ld_step(i) < (isa ? a_rows : b_rows));
+                *reinterpret_cast<i32x4 *>(smem + ld_dst(i) + lane * 16) = v;
             }
         };
 
@@ -329,11 +361,15 @@ struct RingTile {
         i32x4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
         if (tail && e0 == 0)
             reg_tail(KF);
-        else
+        else {
             dma_entry(e0);
+            stage_regs(e0);
+        }
 #pragma unroll
-        for (int e = 1; e < NS - 1; ++e)
+        for (int e = 1; e < NS - 1; ++e) {
             dma_entry(e0 + e);
+            stage_regs(e0 + e);
+        }
         // entry e0 has landed (through LDS DMA, or through registers: lgkmcnt)
         wait_vm_lds<(NS - 2) * NL>();
         lds_barrier();
@@ -371,6 +407,7 @@ struct RingTile {
             }
             mfma_step<P, TM, TN, 0, KA>(fa1, fb1, acc);
             __builtin_amdgcn_sched_barrier(0);
+            stage_regs(e + NS - 1);   // (VGPR-staged variant only) into the free stage
             wait_vm_lds<(NS - 2) * NL>();
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
@@ -402,10 +439,10 @@ struct RingTile {
 };
 
 // Data-parallel kernel: one output tile per workgroup, all of K.
-template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS>
+template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS, int VAR>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p, int tiles_m,
                                                                    int tiles_n) {
-    typedef RingTile<P, BM, BN, BKB, WGM, WGN, NS> RT;
+    typedef RingTile<P, BM, BN, BKB, WGM, WGN, NS, VAR> RT;
     __shared__ __attribute__((aligned(16))) uint8_t smem[RT::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -583,10 +620,10 @@ __device__ __forceinline__ int sk_owner(int64_t x, int64_t iters, int grid) {
 // done sums the contributions in workgroup order (its own from registers),
 // writes the output and resets the counter to zero. Nobody waits on another
 // workgroup, and the summation order does not depend on arrival order.
-template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS>
+template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS, int VAR>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_sk_kernel(GemmProblem p, int tiles_m,
                                                                       int tiles_n, StreamKArgs sk) {
-    typedef RingTile<P, BM, BN, BKB, WGM, WGN, NS> RT;
+    typedef RingTile<P, BM, BN, BKB, WGM, WGN, NS, VAR> RT;
     typedef typename RT::acc_t acc_t;
     constexpr int TM = RT::TM, TN = RT::TN, NT = RT::NT;
     constexpr int SLOT = BM * BN * 4;   // bytes of one partial tile
@@ -801,6 +838,10 @@ static const CfgShape kCfg[CFG_COUNT] = {
     {128, 128, 128, 2, "128x128_bk128_ring2_2blk"},
     {128, 256, 64, 2, "128x256_bk64_ring3_2blk"},
     {256, 256, 128, 1, "256x256_bk128_pingpong"},
+    {256, 256, 128, 1, "256x256_bk128_ring2_split_loaders"},
+    {256, 256, 128, 1, "256x256_bk128_ring2_nt"},
+    {256, 256, 128, 1, "256x256_bk128_ring2_sc1"},
+    {256, 256, 128, 1, "256x256_bk128_ring2_vgpr_staged"},
 };
 
 const char *tile_cfg_name(int cfg) {
@@ -865,7 +906,7 @@ StreamKPlan plan_stream_k(int cfg, int64_t M, int64_t N, int64_t kbytes, int cu_
 template <int P>
 static hipError_t launch_generic(const GemmProblem &p, hipStream_t stream);
 
-template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS>
+template <int P, int BM, int BN, int BKB, int WGM, int WGN, int NS, int VAR = VAR_BASE>
 static hipError_t launch_one(const GemmProblem &p, const StreamKPlan &sk, const TileWorkspace &ws,
                              hipStream_t stream) {
     if (p.kbytes < BKB)   // no full K tile: the ring kernel needs at least one
@@ -884,11 +925,11 @@ static hipError_t launch_one(const GemmProblem &p, const StreamKPlan &sk, const 
         a.partial = ws.partial;
         a.partial_bytes = (int)(2 * (int64_t)sk.grid * BM * BN * 4);
         a.flags = ws.flags;
-        hipLaunchKernelGGL((gemm_tile_sk_kernel<P, BM, BN, BKB, WGM, WGN, NS>), dim3(sk.grid), block,
+        hipLaunchKernelGGL((gemm_tile_sk_kernel<P, BM, BN, BKB, WGM, WGN, NS, VAR>), dim3(sk.grid), block,
                            0, stream, p, tiles_m, tiles_n, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((gemm_tile_kernel<P, BM, BN, BKB, WGM, WGN, NS>), dim3(tiles_m * tiles_n),
+    hipLaunchKernelGGL((gemm_tile_kernel<P, BM, BN, BKB, WGM, WGN, NS, VAR>), dim3(tiles_m * tiles_n),
                        block, 0, stream, p, tiles_m, tiles_n);
     return hipGetLastError();
 }
@@ -936,6 +977,10 @@ static hipError_t launch_prec(int cfg, const GemmProblem &p, const StreamKPlan &
         // stream-K, a partial K tile or the W4A4 epilogue: the ring kernel of
         // the same tile shape
         return launch_one<P, 256, 256, 128, 2, 2, 2>(p, sk, ws, stream);
+    case CFG_256x256_SPLIT: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_SPLIT>(p, sk, ws, stream);
+    case CFG_256x256_NT: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_NT>(p, sk, ws, stream);
+    case CFG_256x256_SC1: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_SC1>(p, sk, ws, stream);
+    case CFG_256x256_VGPR: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_VGPR>(p, sk, ws, stream);
     default: return hipErrorInvalidValue;
     }
 }

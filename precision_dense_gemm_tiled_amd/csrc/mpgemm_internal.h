@@ -41,6 +41,11 @@ enum TileCfg {
     CFG_128x128_2B = 10,    // 4 waves of 64x64, BK = 128 B, 2 stages: 64 KiB, two blocks per CU
     CFG_128x256_2B = 11,    // 4 waves of 64x128, BK = 64 B, 3 stages: 72 KiB, two blocks per CU
     CFG_256x256_PP = 12,    // 8 waves of 128x64 in two ping-pong groups, BK = 128 B, 2 stages
+    // one-change ablations of CFG_256x256_BK128 (the ring kernel's VAR parameter)
+    CFG_256x256_SPLIT = 13, // separate loader wavefronts for A and for B
+    CFG_256x256_NT = 14,    // tile loads non-temporal (nt)
+    CFG_256x256_SC1 = 15,   // tile loads at device scope (sc1)
+    CFG_256x256_VGPR = 16,  // tile loads staged through VGPRs instead of direct-to-LDS
     CFG_COUNT
 };
 

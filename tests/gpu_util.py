@@ -4,8 +4,10 @@ import math
 import numpy as np
 
 # Tile configurations of the GEMM kernels (indices of the MPGEMM_TILE_CFG
-# override): 0-11 the ring kernel's shapes, 12 the 256 x 256 ping-pong kernel.
-N_TILE_CFGS = 13
+# override): 0-11 the ring kernel's shapes, 12 the 256 x 256 ping-pong kernel,
+# 13-16 one-change ablations of the 256 x 256 ring (split loaders, nt, sc1,
+# VGPR-staged loads).
+N_TILE_CFGS = 17
 PINGPONG_CFG = 12
 
 
