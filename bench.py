@@ -14,7 +14,9 @@ size), reported under `per_precision` and `hot_path`.
 Timing: HIP events recorded on the stream the kernels are launched on (torch's
 current stream), W warm-up launches, then K timed launches between two
 synchronisations. Small problems rotate through enough distinct input copies
-that the 256 MB Infinity Cache cannot serve repeats ("cold").
+that the 256 MB Infinity Cache cannot serve repeats ("cold"); their sweep
+entries also carry `us_warm`, the same launches on a single input set that
+stays cached (context only: every throughput and roofline figure is cold).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
                        [--no-cpu-baseline] [--only f16|i8|i4|w4a16|w4a4|quantize] [--eager]
@@ -248,16 +250,27 @@ def sweep_entry(prec, M, N, K, seed, steps, warmup, eager=False):
     del p
     import torch
     torch.cuda.empty_cache()
+    # warm: the same launches on one input set, which then stays in the
+    # Infinity Cache (reported beside the cold figure, never instead of it)
+    t_warm = None
+    if copies > 1 and not eager:
+        pw = Problem(prec, M, N, K, seed, 1)
+        t_warm = time_graph(pw, launches, max(steps, 3))
+        del pw
+        torch.cuda.empty_cache()
     unit = "TFLOP/s" if prec in ("f16", "w4a16") else "TOP/s"
     thr = 2.0 * M * N * K / t / 1e12
     if prec == "quantize":
         unit, thr = "GB/s", algorithmic_bytes(prec, M, N, K) / t / 1e9
-    return {"M": M, "N": N, "K": K, "us": round(t * 1e6, 3),
-            "throughput": round(thr, 3), "unit": unit,
-            "roofline_bound": rf["bound"], "roofline_frac": rf["frac"],
-            "hbm_GBps_algorithmic": round(algorithmic_bytes(prec, M, N, K) / t / 1e9, 1),
-            "input_copies": copies, "launches": reps,
-            "timing": "eager launches" if eager else "hip graph replay"}
+    e = {"M": M, "N": N, "K": K, "us": round(t * 1e6, 3),
+         "throughput": round(thr, 3), "unit": unit,
+         "roofline_bound": rf["bound"], "roofline_frac": rf["frac"],
+         "hbm_GBps_algorithmic": round(algorithmic_bytes(prec, M, N, K) / t / 1e9, 1),
+         "input_copies": copies, "launches": reps,
+         "timing": "eager launches" if eager else "hip graph replay"}
+    if t_warm is not None:
+        e["us_warm"] = round(t_warm * 1e6, 3)
+    return e
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -395,8 +408,9 @@ def main():
                 M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else ((1, s, s) if prec == "quantize" else (s, s, s))
                 idx = CONFIG_INDEX["i8_512"] if (prec == "i8" and s == 512) else CONFIG_INDEX[prec]
                 e = sweep_entry(prec, M, N, K, inputs.config_seed(idx, s), 5, 2, args.eager)
+                warm = f", warm {e['us_warm']} us" if "us_warm" in e else ""
                 log(f"[bench] {prec} {M}x{N}x{K}: {e['us']} us, {e['throughput']} {e['unit']}, "
-                    f"{e['roofline_bound']} frac {e['roofline_frac']}")
+                    f"{e['roofline_bound']} frac {e['roofline_frac']}{warm}")
                 per[prec].append(e)
         result["per_precision"] = per
 
