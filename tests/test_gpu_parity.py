@@ -513,6 +513,28 @@ def test_quantize_edge_values():
     assert np.all(S[0] == 0) and np.all(Q[0] == 0)
 
 
+def test_quantize_many_ties():
+    """Groups whose maximum is exactly 7 s with every other weight (k + 1/2) s:
+    each of those quotients is an exact tie, resolved to the even code; scales
+    with few mantissa bits over many exponents, K = 800 (a partial 512-k
+    segment)."""
+    N, K, G = 64, 800, 32
+    r = np.random.default_rng(11)
+    ng = K // G
+    mant = r.integers(8, 64, (N, ng))                     # at most 6 significant bits
+    expo = r.integers(-14, 6, (N, ng)).astype(np.float64)
+    s = mant * 2.0 ** (expo - 5)
+    k = r.integers(-7, 7, (N, K)).astype(np.float64)
+    W = (k + 0.5) * np.repeat(s, G, axis=1)
+    W[:, ::G] = 7 * s                                     # the group maximum
+    W = W.astype(np.float16)
+    assert np.all(np.isfinite(W))
+    Q, S = _quant(W, G)
+    Qr, Sr = oracle.quantize_w4(W, G)
+    assert np.array_equal(S, Sr.view(np.uint16))
+    assert np.array_equal(Q, Qr)
+
+
 def test_quantize_strided_and_feeds_w4a16():
     """Row strides beyond K on every operand, bytes outside untouched; the
     quantised weights drive the weight-only GEMM to the oracle's result."""
