@@ -881,10 +881,15 @@ StreamKPlan plan_stream_k(int cfg, int64_t M, int64_t N, int64_t kbytes, int cu_
     if (rem == 0)
         return pl;   // whole waves: nothing to balance
     if (mode == SK_MODE_AUTO) {
-        // Split only a short last wave of a grid of at least one full wave:
-        // the split tiles then cost one partial-tile round trip each, against
-        // a last wave that would leave most compute units idle.
-        if (full < 1 || rem * 2 > G)
+        // A split tile's partial sums make a round trip through memory
+        // (written through past the XCD's L2, read back by the finishing
+        // workgroup). Measured on MI355X that costs more than the idle tail
+        // of a short last wave (INT8 6400^3: 32 % slower split), and pays
+        // only when the tiles leave at least 7/8 of the resident workgroup
+        // slots idle and every tile has a long K loop to share out (INT8
+        // 256 x 256 x 65536: 2.1x faster split; 1024 x 1024 x 16384, 256
+        // tiles of 128 stages: 6 % slower).
+        if (T * 8 > G || KT < 128)
             return pl;
     }
     // The last full wave joins the stream-K part, so every workgroup runs

@@ -13,7 +13,7 @@ import pytest
 import oracle
 import precision_dense_gemm_tiled_amd as mp
 from precision_dense_gemm_tiled_amd import inputs
-from tests.gpu_util import dev, f16_tol, freivalds_int, host, require_gpu, sample_rows, N_TILE_CFGS
+from tests.gpu_util import N_TILE_CFGS, dev, f16_tol, host, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -86,28 +86,26 @@ def test_forced_shapes(prec, M, N, K, monkeypatch):
 
 
 @pytest.mark.parametrize("prec", ["i8", "i4", "f16"])
-def test_auto_plan_at_a_ragged_size(prec, monkeypatch):
-    """4352 x 4352 (17 x 17 = 289 tiles of 256 x 256 on 256 compute units): the
-    default plan splits all tiles over the grid. Integer outputs are checked
-    exactly over every element (Freivalds) and equal the data-parallel
-    launch; sampled rows are compared with the oracle."""
-    n, K = 4352, 1024
-    assert mp.mpgemm_plan_gemm({"f16": 0, "i8": 1, "i4": 2}[prec], n, n, K, 256)[2] == 256
-    A, B = inputs.gemm_problem(prec, n, n, K, seed=4352)
+def test_auto_plan_splits_a_long_k(prec, monkeypatch):
+    """256 x 256 x 32768: 16 tiles of 64 x 64, 128 to 512 K stages each; the
+    default plan splits every tile over the grid. Every element is compared
+    with the oracle, and with the data-parallel launch (integers bit for bit)."""
+    M = N = 256
+    K = 32768
+    st, cfg, grid, tdp = mp.mpgemm_plan_gemm({"f16": 0, "i8": 1, "i4": 2}[prec], M, N, K, 256)
+    assert st == 0 and grid > 0 and tdp == 0, (cfg, grid, tdp)
+    A, B = inputs.gemm_problem(prec, M, N, K, seed=256)
     with mp.Handle() as h:
         got = _run(prec, A, B, K, h.value)
     monkeypatch.setenv("MPGEMM_STREAMK", "0")
     with mp.Handle() as h:
         dp = _run(prec, A, B, K, h.value)
-    rows = sample_rows(n, 12, seed=7)
-    _compare(prec, got[rows], _ref(prec, A[rows], B, K), K, f"{prec} {n} sampled rows")
+    _compare(prec, got, _ref(prec, A, B, K), K, f"{prec} {M}x{N}x{K} split")
     if prec == "f16":
         err = np.abs(got.astype(np.float64) - dp.astype(np.float64))
         assert np.all(err <= 2 * f16_tol(K))
     else:
         assert np.array_equal(got, dp)
-        if prec == "i8":
-            freivalds_int(got, A, B, seed=1)
 
 
 def test_graph_replays_match_eager(monkeypatch):

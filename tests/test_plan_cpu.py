@@ -109,15 +109,20 @@ def test_stream_k_partition_invariants():
 
 
 def test_stream_k_plan(mp):
-    """Auto policy: a stream-K grid only for a short last wave (at most half a
-    wave of tiles) after at least one full wave; the last full wave joins the
-    split part; the partial tiles fit the handle's workspace."""
+    """Auto policy: a stream-K grid only when the tiles fill at most an eighth
+    of the resident workgroups and each tile has at least 128 K stages; then
+    every tile is split (no data-parallel part) over min(iterations, G)
+    workgroups, and the partial tiles fit the handle's workspace."""
     rng = np.random.default_rng(3)
     seen = 0
-    for _ in range(2000):
+    for i in range(3000):
         prec = int(rng.integers(0, 4))
-        M, N = (int(v) for v in rng.integers(1, 12000, 2))
-        K = int(rng.integers(1, 9000)) * 2
+        if i % 2:   # small outputs with long K, where splitting can pay
+            M, N = (int(v) for v in rng.integers(1, 1500, 2))
+            K = int(rng.integers(1, 40000)) * 2
+        else:
+            M, N = (int(v) for v in rng.integers(1, 12000, 2))
+            K = int(rng.integers(1, 9000)) * 2
         st, cfg, grid, tdp = mp.mpgemm_plan_gemm(prec, M, N, K, 256)
         assert st == OK
         BM, BN, BKB, per_cu = TILE[cfg]
@@ -126,20 +131,23 @@ def test_stream_k_plan(mp):
         KT = -(-KBYTES[prec](K) // BKB)
         if grid == 0:
             assert tdp == 0
-            assert T % G == 0 or T < G or 2 * (T % G) > G or KT < 2 or KBYTES[prec](K) < BKB
+            assert 8 * T > G or KT < 128 or KBYTES[prec](K) < BKB
             continue
         seen += 1
-        full, rem = divmod(T, G)
-        assert full >= 1 and 0 < 2 * rem <= G
-        assert tdp == (full - 1) * G and grid == G
+        assert 8 * T <= G and KT >= 128
+        assert tdp == 0 and grid == min(T * KT, G)
         assert 2 * grid * BM * BN * 4 <= WORKSPACE_BYTES
     assert seen > 20
 
 
-def test_stream_k_at_a_ragged_size(mp):
-    """N = 6144 FP16: 576 tiles of 256 x 256 are 2.25 waves on 256 compute
-    units; the plan runs one wave whole and splits the other 320 tiles."""
-    assert mp.mpgemm_plan_gemm(0, 6144, 6144, 6144, 256) == (OK, 4, 256, 256)
+def test_stream_k_policy_examples(mp):
+    """N = 6144 FP16 (2.25 waves of 256 x 256 tiles) and N = 4352 INT8 (1.13
+    waves) run data-parallel: splitting the short last wave was measured
+    slower. 256 x 256 x 65536 INT8 (16 tiles of 64 x 64, 512 stages each) is
+    split over all 768 resident workgroups."""
+    assert mp.mpgemm_plan_gemm(0, 6144, 6144, 6144, 256) == (OK, 4, 0, 0)
+    assert mp.mpgemm_plan_gemm(1, 4352, 4352, 4352, 256) == (OK, 4, 0, 0)
+    assert mp.mpgemm_plan_gemm(1, 256, 256, 65536, 256) == (OK, 2, 768, 0)
 
 
 def test_plan_gemm_arguments(mp):
