@@ -134,6 +134,31 @@ def test_i8_extremes():
     assert np.all(_run("i8", full, top, K) == -128 * 127 * K)
 
 
+@pytest.mark.parametrize("streamk", ["0", "auto"])
+def test_integer_k_bound(streamk, monkeypatch):
+    """The largest K the integer calls accept: INT8 at K = 131071 (all -128:
+    every sum 16384 K = 2^31 - 16384; K tail of 127 bytes) and INT4 at
+    K = 131070 (all -8: the widened operands sum 256 * 64 K = 2^31 - 32768
+    inside the kernel before the shift), plus random values against the
+    oracle; data-parallel and with the default plan (which splits these long
+    K loops over the grid)."""
+    if streamk == "0":
+        monkeypatch.setenv("MPGEMM_STREAMK", "0")
+    with mp.Handle() as h:
+        K = 131071
+        m128 = np.full((40, K), -128, dtype=np.int8)
+        c = host(mp.gemm_i8(dev(m128), dev(m128), handle=h.value))
+        assert np.all(c == 16384 * K) and 16384 * K < 2 ** 31
+        A, B = inputs.gemm_problem("i8", 33, 70, K, seed=131071)
+        assert np.array_equal(host(mp.gemm_i8(dev(A), dev(B), handle=h.value)), oracle.gemm_i8(A, B))
+        K = 131070
+        m8 = pack_i4(np.full((40, K), -8))
+        c = host(mp.gemm_i4(dev(m8), dev(m8), K, handle=h.value))
+        assert np.all(c == 64 * K) and 256 * 64 * K < 2 ** 31
+        A, B = inputs.gemm_problem("i4", 33, 70, K, seed=131070)
+        assert np.array_equal(host(mp.gemm_i4(dev(A), dev(B), K, handle=h.value)), oracle.gemm_i4(A, B, K))
+
+
 def test_f16_small_integers_bit_exact():
     """Integers in [-4, 4]: every partial sum is an integer below 2^24, so an
     fp32 accumulator is exact in any order and C must equal the INT8 oracle."""
