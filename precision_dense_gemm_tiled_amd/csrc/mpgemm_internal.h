@@ -114,6 +114,8 @@ enum W4A16Cfg {
     W4A16_SLICE_32x32_K2 = 9,  // ... 32 x 32 tile, 2 column x 2 K wavefronts
     W4A16_SLICE_64x128 = 10,   // ... 64 x 128 tile
     W4A16_SLICE_128x128 = 11,  // ... 128 x 128 tile
+    W4A16_RING3_128x64 = 12,   // MFMA, 128 x 64 tile, activations and weights through a 3-stage LDS ring
+    W4A16_RING4_128x64 = 13,   // ... 4-stage ring
     W4A16_CFG_COUNT
 };
 

@@ -24,6 +24,7 @@
 #include "lds_dma.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <climits>
 
 namespace mpg {
@@ -32,6 +33,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // 8 packed nibbles (k = 0..7, low nibble first) -> 8 fp16 values of q in the
 // order k = 0,4,1,5,2,6,3,7.
@@ -384,10 +386,40 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(W4A16Problem p, int lg)
 // also split over KS workgroups: each writes its fp32 partial tile to the
 // workspace and a second kernel adds the slices in slice order.
 
-__device__ __forceinline__ f16x8 dequant8_natural(uint32_t w, _Float16 scale) {
+// 8 packed nibbles (k = 0..7, low nibble first) -> 8 fp16 values q * s in
+// natural k order, 18 VALU operations: the even-k nibbles stay at bits 0-3 of
+// each byte, the odd-k ones at bits 4-7; one byte permute per pair builds
+// (nibble, 0, nibble << 4, 0), and one XOR flips the sign bit of both (u =
+// nibble ^ 8 = q + 8) and sets the exponents that make the halves read
+// 1024 + u and 64 + u'; subtracting (1032, 72) leaves q exactly.
+__device__ __forceinline__ f16x8 dequant8_perm(uint32_t w, f16x2 s2) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = w & 0xF0F0F0F0u;
+    const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-72.0f};
+    f16x2 q[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        // result bytes: lo.b, 0, hi.b, 0 (v_perm: src1 = bytes 0-3, src0 = 4-7, selector 12 = zero)
+        const uint32_t sel = (uint32_t)b | (12u << 8) | ((4u + b) << 16) | (12u << 24);
+        const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) ^ 0x54806408u;
+        q[b] = (__builtin_bit_cast(f16x2, pr) + bias) * s2;
+    }
+    return f16x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+}
+
+// Consecutive workgroup ids go round-robin over the 8 XCDs; renumber them so
+// that each XCD gets a contiguous range of logical ids (neighbouring K slices
+// and tiles then share that XCD's L2).
+__device__ __forceinline__ int xcd_contiguous(int id, int nblk) {
+    if (nblk < 8)
+        return id;
+    const int xcd = id % 8, local = id / 8;
+    const int base = nblk / 8, rem = nblk % 8;
+    return xcd * base + (xcd < rem ? xcd : rem) + local;
+}
+
+__device__ __forceinline__ f16x8 dequant8_natural(uint32_t w, f16x2 s2) {
     const uint32_t u = w ^ 0x88888888u;
     const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-72.0f};
-    const f16x2 s2 = {scale, scale};
     f16x2 q[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -412,15 +444,7 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
     // Workgroup -> (column group, row block, K slice). Consecutive workgroup
     // ids go round-robin over the 8 XCDs; give each XCD a contiguous range so
     // the K slices and row blocks of one column group share an L2.
-    int logical = blockIdx.x;
-    {
-        const int nblk = gridDim.x;
-        if (nblk >= 8) {
-            const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
-            const int base = nblk / 8, rem = nblk % 8;
-            logical = xcd * base + (xcd < rem ? xcd : rem) + local;
-        }
-    }
+    const int logical = xcd_contiguous(blockIdx.x, gridDim.x);
     const int ks = logical % sk.ks;
     const int tile = logical / sk.ks;          // = ng * mblocks + mb
     const int mb = tile % sk.mblocks, ng = tile / sk.mblocks;
@@ -495,7 +519,8 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
             for (int j = 0; j < NB; ++j) {
                 // a run past the K range gets q = 0 (u = 8 in every nibble)
                 const uint32_t w = live ? (uint32_t)wr[s][j][t] : 0u;
-                const f16x8 b = dequant8_natural(w, __builtin_bit_cast(_Float16, sr[s][j]));
+                const _Float16 sc = __builtin_bit_cast(_Float16, sr[s][j]);
+                const f16x8 b = dequant8_natural(w, f16x2{sc, sc});
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b, acc[i][j], 0, 0, 0);
@@ -578,6 +603,439 @@ __global__ __launch_bounds__(256) void w4a16_reduce_kernel(W4A16Problem p, W4A16
         p.Y[(int64_t)m * p.ldy + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
 }
 
+// ---------------------------------------------------------------------------
+// Larger M: w4a16_ring_kernel. One 128 x 64 output tile per workgroup. The
+// activations stream through a ring of LDS stages (128 rows x 128 k, 32 KiB)
+// next to the tile's packed weights (64 rows x 128 k, 4 KiB), both moved by
+// direct-to-LDS loads. Within a stage each of the 4 wavefronts takes 32 k for
+// all 128 rows, so every dequantised weight word feeds 4 MFMAs
+// (v_mfma_f32_32x32x16_f16); the 4 partial tiles meet in LDS at the end.
+// When the tiles alone would leave compute units idle, K is also split over
+// KS workgroups: each writes an fp32 slice of Y (row-major, padded to whole
+// tiles) and w4a16_rowsum_kernel adds the slices in slice order.
+//
+// k order inside a wavefront's 32 k (four runs of 8): at MFMA step t (0, 1)
+// lane half h = l / 32 supplies run 2h + t of both operands, so a lane gets
+// its two weight words of a column with one 8-byte LDS read.
+//
+// LDS layouts (16-byte chunks): activation row r holds its 16 chunks with
+// chunk c at slot c ^ (r & 15); weight row n holds 4 chunks (32 k each) with
+// chunk c at slot c ^ ((n / 4) & 3). Fragment reads are then free of bank
+// conflicts, and the direct-to-LDS loads, which write lane-contiguous 16-byte
+// slots, fetch the permuted global chunk instead.
+constexpr int RG_BM = 128, RG_BN = 64, RG_BK = 128;
+constexpr int RG_XST = RG_BM * RG_BK * 2;            // activation bytes per stage
+constexpr int RG_WST = RG_BN * RG_BK / 2;            // packed weight bytes per stage
+constexpr int RG_STAGE = RG_XST + RG_WST;
+constexpr int RG_RED = 4 * 32 * 64 * 16;             // the 4 wavefronts' fp32 tiles
+constexpr int RG_PER = RG_XST / (256 * 16) + 1;      // direct-to-LDS loads per thread per stage
+
+// LDS of one workgroup: NSTG ring slots, then a table of fp16 scales (spr
+// entries per weight row, what is left of the 160 KiB). The epilogue's 4
+// partial tiles (32 KiB each) reuse the ring and, with 3 stages, the table.
+template <int NSTG>
+struct RingLds {
+    static constexpr int spr = NSTG == 3 ? 384 : 128;
+    static constexpr int ring = NSTG * RG_STAGE;
+    static constexpr int bytes = ring + RG_BN * spr * 2;
+    static_assert(bytes <= 160 * 1024 && bytes >= RG_RED, "LDS");
+};
+static int ring_spr(int cfg) { return cfg == W4A16_RING3_128x64 ? RingLds<3>::spr : RingLds<4>::spr; }
+
+// A 16-byte direct-to-LDS load (lane l writes lds + 16 l) issued through
+// inline assembly, so the compiler neither counts it nor waits for it before
+// LDS reads: every consumer waits with wait_vm_lds<> and a barrier. (The
+// compiler's own tracking of such loads cannot tell ring slots apart and
+// would wait for all of them before any read.)
+// M0 (the LDS base of the load) is saved and restored around it.
+__device__ __forceinline__ void dma16_untracked(const void *g, const void *lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(g), "s"(base)
+                 : "memory");
+}
+// The same with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (global_load_lds_dwordx4 v_off, s_base): no per-lane address
+// arithmetic when only the base moves.
+__device__ __forceinline__ void dma16_untracked_sb(uint32_t voff, const void *sbase, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(voff), "s"(sbase), "s"(lds_base)
+                 : "memory");
+}
+// A 2-byte global load into a VGPR, untracked likewise: its value may be used
+// only after a wait that covers it and untracked_ready().
+__device__ __forceinline__ uint32_t load_u16_untracked(const uint16_t *g) {
+    uint32_t v;
+    asm volatile("global_load_ushort %0, %1, off" : "=v"(v) : "v"(g) : "memory");
+    return v;
+}
+__device__ __forceinline__ void untracked_ready(uint32_t &v) { asm volatile("" : "+v"(v)); }
+
+// s_waitcnt for "at most `ahead` stages of direct-to-LDS loads still in
+// flight" (0 <= ahead <= NSTG).
+template <int NSTG>
+__device__ __forceinline__ void ring_wait(int ahead) {
+    if constexpr (NSTG >= 4) {
+        if (ahead >= 4) {
+            wait_vm_lds<4 * RG_PER>();
+            return;
+        }
+    }
+    if (ahead >= 3)
+        wait_vm_lds<3 * RG_PER>();
+    else if (ahead == 2)
+        wait_vm_lds<2 * RG_PER>();
+    else if (ahead == 1)
+        wait_vm_lds<RG_PER>();
+    else
+        wait_vm_lds<0>();
+}
+
+// One wavefront's operands of one stage: activation fragments a[t][i] and
+// packed weight words with their scales (before dequantisation), and the
+// dequantised weight fragments b[t][j].
+struct RingRaw {
+    f16x8 a[2][4];
+    uint32_t wq[2][2];
+    f16x2 sc[2];   // the group scale in both halves
+};
+struct RingFrag {
+    f16x8 a[2][4];
+    f16x8 b[2][2];
+};
+
+template <int NSTG>
+__global__ __launch_bounds__(256) void w4a16_ring_kernel(W4A16Problem p, W4A16Split sk, int lg) {
+    static_assert(NSTG == 3 || NSTG == 4, "ring depth");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[RingLds<NSTG>::bytes];
+    uint16_t *tab = reinterpret_cast<uint16_t *>(smem + RingLds<NSTG>::ring);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+    const int logical = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int ks = logical % sk.ks, tile = logical / sk.ks;
+    const int mb = tile % sk.mblocks, ng = tile / sk.mblocks;
+    const int m0 = mb * RG_BM, n0 = ng * RG_BN;
+    const int k_begin = ks * sk.kslice;
+    const int k_end = min(p.K, k_begin + sk.kslice);
+    const int nst = (k_end - k_begin + RG_BK - 1) / RG_BK;    // stages (the last may be partial)
+    const int nfull = (k_end - k_begin) / RG_BK;               // whole stages
+    auto kstage = [&](int t) { return k_begin + t * RG_BK; };   // first k of stage t
+
+    // scale table tab[(g - g0) * 64 + n] (group-major: the lanes of a read
+    // take consecutive columns), first pass (up to 64 groups: 16 per
+    // thread), loaded ahead of the ring so that it lands with stage 0
+    const int g0 = k_begin >> lg;
+    const int gcnt = ((k_end - 1) >> lg) - g0 + 1;
+    const int wcol = tid >> 2;
+    const uint16_t *srow = p.S + (int64_t)min(n0 + wcol, p.N - 1) * p.lds + g0;
+    uint32_t sv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        sv[e] = load_u16_untracked(srow + min((tid & 3) + 4 * e, gcnt - 1));
+
+    // direct-to-LDS sources: 8 activation chunks (4 rows per wavefront
+    // instruction) and 1 weight chunk per thread and stage. Rows past M or N
+    // are clamped (their results are never stored); k is clamped to K (runs
+    // past the slice are zeroed before use).
+    const int xk = 8 * ((lane & 15) ^ ((4 * wave + (lane >> 4)) & 15));
+    const uint16_t *xrow[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const int r = 4 * (wave + 4 * v) + (lane >> 4);
+        xrow[v] = p.X + (int64_t)min(m0 + r, p.M - 1) * p.ldx;
+    }
+    const int wk = 32 * ((tid & 3) ^ ((wcol >> 2) & 3));
+    const uint8_t *wrow = p.W + (int64_t)min(n0 + wcol, p.N - 1) * p.ldw_b;
+    // whole stages (k0 + 128 <= K): uniform bases plus per-lane byte offsets
+    // that stay fixed (the host keeps 128 ldx * 2 and 64 ldw_b below 2^32)
+    uint32_t xoff[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+        xoff[v] = (uint32_t)((xrow[v] - p.X - (int64_t)m0 * p.ldx + xk) * 2);
+    const uint32_t woff = (uint32_t)((wrow - p.W) - (int64_t)n0 * p.ldw_b + (wk >> 1));
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)smem;
+    const uint32_t wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto issue = [&](int q, int s) {   // stage s into ring slot q
+        const int k0 = kstage(s);
+        const uint32_t lslot = lds0 + q * RG_STAGE + wave_u * 1024;
+        if (k0 + RG_BK <= p.K) {
+            const uint16_t *xb = p.X + (int64_t)m0 * p.ldx + k0;
+            const uint8_t *wb = p.W + (int64_t)n0 * p.ldw_b + (k0 >> 1);
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+                dma16_untracked_sb(xoff[v], xb, lslot + 4 * v * 1024);
+            dma16_untracked_sb(woff, wb, lslot + RG_XST);
+        } else {
+            const uint8_t *base = smem + q * RG_STAGE;
+            const int kx = min(k0 + xk, p.K - 8);
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+                dma16_untracked(xrow[v] + kx, base + (wave + 4 * v) * 1024);
+            dma16_untracked(wrow + (min(k0 + wk, p.K - 32) >> 1), base + RG_XST + wave * 1024);
+        }
+    };
+    // fill the whole ring: stage s + NSTG later goes into the slot of stage s
+    // once every wavefront has read stage s
+    const int pre = min(nst, NSTG);
+    for (int q = 0; q < pre; ++q)
+        issue(q, q);
+
+    // stage 0 (and, being older, the scale loads) landed
+    ring_wait<NSTG>(pre - 1);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        untracked_ready(sv[e]);
+        const int g = (tid & 3) + 4 * e;
+        if (g < gcnt)
+            tab[g * RG_BN + wcol] = (uint16_t)sv[e];
+    }
+    // more than 64 groups: further passes (their loads are tracked, so the
+    // compiler waits for them, and with them for the ring)
+    for (int e0 = 64; e0 < gcnt; e0 += 64) {
+        uint16_t v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            v[e] = srow[min(e0 + (tid & 3) + 4 * e, gcnt - 1)];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int g = e0 + (tid & 3) + 4 * e;
+            if (g < gcnt)
+                tab[g * RG_BN + wcol] = v[e];
+        }
+        wait_vm_lds<0>();   // no tracked load left in flight past this point
+    }
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.f;
+
+    const int xa = (lane & 31) * 256;     // this lane's activation row within a 32-row block
+    // LDS reads of this wavefront's 32 k of stage s (in ring slot q); with
+    // TAIL, runs past the slice read as zeros
+    auto read_raw = [&](int q, int s, auto tail) {
+        constexpr bool TAIL = decltype(tail)::value;
+        const uint8_t *base = smem + q * RG_STAGE;
+        const int kw = kstage(s) + 32 * wave;
+        const bool live = !TAIL || kw < k_end;
+        RingRaw R;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = 32 * j + (lane & 31);
+            const uint64_t d = *reinterpret_cast<const uint64_t *>(
+                base + RG_XST + col * 64 + 16 * (wave ^ ((col >> 2) & 3)) + 8 * h);
+            R.wq[j][0] = live ? (uint32_t)d : 0u;
+            R.wq[j][1] = live ? (uint32_t)(d >> 32) : 0u;
+            const _Float16 sc = __builtin_bit_cast(_Float16, tab[(((live ? kw : k_begin) >> lg) - g0) * RG_BN + col]);
+            R.sc[j] = f16x2{sc, sc};
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int xc = 16 * ((4 * wave + 2 * h + t) ^ (lane & 15));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                R.a[t][i] = *reinterpret_cast<const f16x8 *>(base + i * 32 * 256 + xa + xc);
+                if constexpr (TAIL)
+                    R.a[t][i] = live ? R.a[t][i] : f16x8{};
+            }
+        }
+        return R;
+    };
+    auto dequant = [&](const RingRaw &R, RingFrag &F) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                F.a[t][i] = R.a[t][i];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                F.b[t][j] = dequant8_perm(R.wq[j][t], R.sc[j]);
+        }
+    };
+    auto mfma = [&](const RingFrag &F) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[t][i], F.b[t][j], acc[i][j], 0, 0, 0);
+    };
+
+    RingFrag F0, F1;
+    lds_barrier();   // stage 0 and the scale table visible
+    if (0 < nfull)
+        dequant(read_raw(0, 0, std::false_type{}), F0);
+    else
+        dequant(read_raw(0, 0, std::true_type{}), F0);
+
+    // One step (stage s in `cur`, in ring slot q): wait until stage s + 1 has
+    // landed and publish it (the barrier also certifies that every wavefront
+    // has read stage s), refill slot q with stage s + NSTG, read stage s + 1,
+    // then the MFMAs of stage s with the dequantisation of stage s + 1 in
+    // their shadow. The steady form runs only where the refill is real and
+    // stage s + 1 whole, so exactly NSTG - 2 stages after s + 1 are in flight
+    // at the wait; it has no branch (the accumulators stay in place).
+    int q = 0;
+    auto next_slot = [&](int x) { return x + 1 == NSTG ? 0 : x + 1; };
+    // The 9 direct-to-LDS loads of the refill are spread over the 16 MFMAs
+    // (one per MFMA pair, in explicit scheduling segments): issued together,
+    // they queue in the compute unit's load path and stall the in-order
+    // instruction stream with the matrix unit idle.
+    auto step_steady = [&](int s, const RingFrag &cur, RingFrag &nxt) {
+        wait_vm_lds<(NSTG - 2) * RG_PER>();
+        lds_barrier();
+        const int qn = next_slot(q);
+        __builtin_amdgcn_sched_barrier(0);
+        const RingRaw R = read_raw(qn, s + 1, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        // the refill is a whole stage (the steady condition keeps it below nfull)
+        const int k0 = kstage(s + NSTG);
+        const uint32_t lslot = lds0 + q * RG_STAGE + wave_u * 1024;
+        const uint16_t *xb = p.X + (int64_t)m0 * p.ldx + k0;
+        const uint8_t *wb = p.W + (int64_t)n0 * p.ldw_b + (k0 >> 1);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            dma16_untracked_sb(xoff[g], xb, lslot + 4 * g * 1024);
+            __builtin_amdgcn_sched_barrier(0);
+            const int t = g / 4, j = (g / 2) % 2, i0 = 2 * (g % 2);
+            acc[i0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[t][i0], cur.b[t][j], acc[i0][j], 0, 0, 0);
+            acc[i0 + 1][j] =
+                __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[t][i0 + 1], cur.b[t][j], acc[i0 + 1][j], 0, 0, 0);
+            if (g >= 4) {
+                const int tt = (g - 4) / 2, jj = (g - 4) % 2;
+                nxt.b[tt][jj] = dequant8_perm(R.wq[jj][tt], R.sc[jj]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        dma16_untracked_sb(woff, wb, lslot + RG_XST);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                nxt.a[t][i] = R.a[t][i];
+        q = qn;
+    };
+    int s = 0;
+    for (; s + 1 + NSTG < nfull; s += 2) {
+        step_steady(s, F0, F1);
+        step_steady(s + 1, F1, F0);
+    }
+    // drain: at most NSTG + 2 stages remain, stage s in F0; after the last
+    // stage the reads are of a stale slot and their result is unused
+    auto step_drain = [&](int x, const RingFrag &cur, RingFrag &nxt) {
+        ring_wait<NSTG>(max(0, min(NSTG - 2, nst - x - 2)));
+        lds_barrier();
+        if (x + NSTG < nst)
+            issue(q, x + NSTG);
+        q = next_slot(q);
+        const RingRaw R = read_raw(q, x + 1, std::true_type{});
+        mfma(cur);
+        dequant(R, nxt);
+    };
+    if (s < nst)
+        step_drain(s, F0, F1);
+    if (s + 1 < nst)
+        step_drain(s + 1, F1, F0);
+    if (s + 2 < nst)
+        step_drain(s + 2, F0, F1);
+    if (s + 3 < nst)
+        step_drain(s + 3, F1, F0);
+    if (s + 4 < nst)
+        step_drain(s + 4, F0, F1);
+    if constexpr (NSTG == 4)
+        if (s + 5 < nst)
+            step_drain(s + 5, F1, F0);
+
+    // the 4 partial tiles meet in LDS (every load has landed, the ring is
+    // free): wavefront w leaves the row blocks of the other three in its
+    // 32 KiB, wavefront v then adds the 4 partials of row block v in
+    // wavefront order
+    __syncthreads();
+    f32x4 *red = reinterpret_cast<f32x4 *>(smem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (i != wave)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+                    red[(wave * 32 + (i * 2 + j) * 4 + qq) * 64 + lane] =
+                        f32x4{acc[i][j][4 * qq], acc[i][j][4 * qq + 1], acc[i][j][4 * qq + 2], acc[i][j][4 * qq + 3]};
+    __syncthreads();
+    // 32x32 accumulator layout: register r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
+    // column l % 32
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int f = (wave * 2 + j) * 4 + qq;
+            f32x4 own{};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i == wave)
+                    own = f32x4{acc[i][j][4 * qq], acc[i][j][4 * qq + 1], acc[i][j][4 * qq + 2], acc[i][j][4 * qq + 3]};
+            f32x4 y = wave == 0 ? own : red[f * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < 4; ++w)
+                y += wave == w ? own : red[(w * 32 + f) * 64 + lane];
+            const int ml = 32 * wave + 8 * qq + 4 * h;
+            const int n = n0 + 32 * j + (lane & 31);
+            if (sk.ks == 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = m0 + ml + e;
+                    if (m < p.M && n < p.N)
+                        p.Y[(int64_t)m * p.ldy + n] = __builtin_bit_cast(uint16_t, (_Float16)y[e]);
+                }
+            } else {
+                const int64_t pn = (int64_t)sk.ngroups * RG_BN;
+                float *dst = sk.partial + ((int64_t)ks * sk.mblocks * RG_BM + m0 + ml) * pn + n;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[e * pn] = y[e];
+            }
+        }
+}
+
+// Y = fp16(sum of the KS row-major fp32 slices written by w4a16_ring_kernel),
+// slices added in slice order; one thread per 4 consecutive columns.
+__global__ __launch_bounds__(256) void w4a16_rowsum_kernel(W4A16Problem p, W4A16Split sk) {
+    const int qpr = (p.N + 3) / 4;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)p.M * qpr)
+        return;
+    const int m = (int)(e / qpr), n = (int)(e % qpr) * 4;
+    const int64_t pn = (int64_t)sk.ngroups * RG_BN;
+    const int64_t slice = (int64_t)sk.mblocks * RG_BM * pn;
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(sk.partial + (int64_t)m * pn + n);
+    f32x4 y = src[0];
+    for (int o = 1; o < sk.ks; ++o)
+        y += src[o * (slice / 4)];
+    uint16_t *dst = p.Y + (int64_t)m * p.ldy + n;
+    if (n + 4 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        const f16x4 o = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+        *reinterpret_cast<f16x4 *>(dst) = o;
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (n + c < p.N)
+                dst[c] = __builtin_bit_cast(uint16_t, (_Float16)y[c]);
+    }
+}
+
 
 template <int MT, int WN, int WK, int U>
 static hipError_t launch_cfg(const W4A16Problem &p, hipStream_t stream, int lg) {
@@ -634,6 +1092,33 @@ static hipError_t launch_slice(const W4A16Problem &p, const W4A16Plan &plan, con
     return hipGetLastError();
 }
 
+template <int MT, int WN, int WK, int U>
+static hipError_t launch_cfg(const W4A16Problem &p, hipStream_t stream, int lg);
+
+template <int NSTG>
+static hipError_t launch_ring(const W4A16Problem &p, const W4A16Plan &plan, const W4A16Workspace &ws,
+                              hipStream_t stream, int lg) {
+    // the ring kernel's per-lane load offsets are 32-bit: 128 activation rows
+    // and 64 weight rows of the strides must span less than 4 GiB
+    if (p.ldx * 2 * RG_BM >= ((int64_t)1 << 32) || p.ldw_b * RG_BN >= ((int64_t)1 << 32))
+        return launch_cfg<2, 4, 1, 2>(p, stream, lg);
+    W4A16Split sk;
+    sk.mblocks = plan.mblocks;
+    sk.ngroups = plan.ngroups;
+    sk.ks = plan.ks;
+    sk.kslice = plan.kslice;
+    sk.partial = ws.partial;
+    const int64_t blocks = (int64_t)sk.mblocks * sk.ngroups * sk.ks;
+    if (blocks > INT_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((w4a16_ring_kernel<NSTG>), dim3((unsigned)blocks), dim3(256), 0, stream, p, sk, lg);
+    if (sk.ks == 1)
+        return hipGetLastError();
+    const int64_t threads = (int64_t)p.M * ((p.N + 3) / 4);
+    hipLaunchKernelGGL(w4a16_rowsum_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p, sk);
+    return hipGetLastError();
+}
+
 // The slice configurations: (configuration, MB, NB, WN, WK, NST). One list
 // feeds both the host planning and the kernel dispatch.
 #define MPG_SLICE_CONFIGS(X)                 \
@@ -650,6 +1135,29 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cfg, int cu_count, int
     case C: MB = mb; NB = nb; WN = wn; WK = wk; NST = nst; break;
         MPG_SLICE_CONFIGS(MPG_SHAPE)
 #undef MPG_SHAPE
+    case W4A16_RING3_128x64:
+    case W4A16_RING4_128x64: {
+        plan.mblocks = (int)((M + RG_BM - 1) / RG_BM);
+        plan.ngroups = (int)((N + RG_BN - 1) / RG_BN);
+        const int64_t tiles = (int64_t)plan.mblocks * plan.ngroups;
+        const int64_t steps = (K + RG_BK - 1) / RG_BK;
+        int64_t ks = 1;
+        while (tiles * ks < cu_count && ks < steps)
+            ++ks;
+        // equal slices in whole stages; a slice touches at most 4 spk + 1
+        // groups (G >= 32), which the LDS scale table must hold
+        int64_t spk = (steps + ks - 1) / ks;
+        spk = std::min<int64_t>(spk, (ring_spr(plan.cfg) - 1) / 4);
+        ks = (steps + spk - 1) / spk;
+        if (ks > 1 && ks * plan.mblocks * RG_BM * plan.ngroups * RG_BN > partial_floats) {
+            plan.cfg = W4A16_MFMA_TILE;
+            plan.mblocks = plan.ngroups = 0;
+            return plan;
+        }
+        plan.ks = (int)ks;
+        plan.kslice = (int)(RG_BK * spk);
+        return plan;
+    }
     default: return plan;   // GEMV and the older MFMA kernels split K inside the workgroup
     }
     const int64_t BM = 16 * MB, BN = 16 * NB * WN, KSPAN = 128 * NST * WK;
@@ -682,14 +1190,16 @@ const char *w4a16_cfg_name(int cfg) {
         "mfma 16 rows x 16 cols, K split 4", "mfma 32 x 64 tile",
         "gemv R1 KS2", "gemv R2 KS2", "gemv R4 KS2", "gemv R2 KS1", "gemv R4 KS1", "gemv R8 KS1",
         "slice 16 x 16, K over 4 wavefronts", "slice 32 x 32, K over 2 wavefronts",
-        "slice 64 x 128", "slice 128 x 128"};
+        "slice 64 x 128", "slice 128 x 128", "ring 128 x 64, 3 stages", "ring 128 x 64, 4 stages"};
     return cfg >= 0 && cfg < W4A16_CFG_COUNT ? names[cfg] : "?";
 }
 
 int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K) {
     (void)N;
     (void)K;
-    // measured at N = K = 4096 (cold weights)
+    // measured at N = K = 4096 (cold weights, HIP graph replay): the ring
+    // kernel ties the 64 x 128 slices at M = 128 (19.6 vs 19.2 us) and wins
+    // from M = 192 on (22 vs 30 us; 29 vs 66 at 512, 82 vs 283 at 1024)
     if (M == 1)
         return W4A16_GEMV_R2_KS2;
     if (M <= 4)
@@ -698,7 +1208,9 @@ int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K) {
         return W4A16_SLICE_16x16_K4;
     if (M <= 64)
         return W4A16_SLICE_32x32_K2;
-    return W4A16_SLICE_64x128;
+    if (M <= 128)
+        return W4A16_SLICE_64x128;
+    return W4A16_RING3_128x64;
 }
 
 static hipError_t launch_one(const W4A16Problem &p, const W4A16Plan &plan, const W4A16Workspace &ws,
@@ -716,6 +1228,8 @@ static hipError_t launch_one(const W4A16Problem &p, const W4A16Plan &plan, const
     case C: return launch_slice<mb, nb, wn, wk, nst>(p, plan, ws, stream, lg);
         MPG_SLICE_CONFIGS(MPG_LAUNCH)
 #undef MPG_LAUNCH
+    case W4A16_RING3_128x64: return launch_ring<3>(p, plan, ws, stream, lg);
+    case W4A16_RING4_128x64: return launch_ring<4>(p, plan, ws, stream, lg);
     default: return hipErrorInvalidValue;
     }
 }
