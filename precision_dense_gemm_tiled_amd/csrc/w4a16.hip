@@ -782,13 +782,16 @@ __global__ __launch_bounds__(256) void w4a16_ring_kernel(W4A16Problem p, W4A16Sp
         }
     };
     // fill the whole ring: stage s + NSTG later goes into the slot of stage s
-    // once every wavefront has read stage s
-    const int pre = min(nst, NSTG);
-    for (int q = 0; q < pre; ++q)
-        issue(q, q);
+    // once every wavefront has read stage s. All NSTG slots are loaded even
+    // when the slice has fewer stages (copies of its last stage, never read):
+    // with no branch between the untracked scale loads above and their use
+    // below, the compiler cannot merge their registers with early copies.
+#pragma unroll
+    for (int q = 0; q < NSTG; ++q)
+        issue(q, min(q, nst - 1));
 
     // stage 0 (and, being older, the scale loads) landed
-    ring_wait<NSTG>(pre - 1);
+    wait_vm_lds<(NSTG - 1) * RG_PER>();
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         untracked_ready(sv[e]);
