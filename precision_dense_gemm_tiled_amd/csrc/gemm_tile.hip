@@ -242,7 +242,7 @@ __device__ __forceinline__ void stage_factors(const GemmProblem &p, int row0, in
 // non-temporal (nt); 3 the tile loads at device scope (sc1); 4 tile loads
 // staged through VGPRs (global_load_dwordx4, then ds_write_b128 into the free
 // stage before the barrier that publishes it) instead of direct-to-LDS.
-enum { VAR_BASE = 0, VAR_SPLIT = 1, VAR_NT = 2, VAR_SC1 = 3, VAR_VGPR = 4 };
+enum { VAR_BASE = 0, VAR_SPLIT = 1, VAR_NT = 2, VAR_SC1 = 3, VAR_VGPR = 4, VAR_SPREAD = 5 };
 
 template <int AUX>
 __device__ __forceinline__ void dma16_cp(const void *g, void *lds) {
@@ -261,6 +261,9 @@ struct RingTile {
     static constexpr int NL = A_PER_T + B_PER_T;   // direct-to-LDS loads per thread per tile
     static constexpr bool SPLIT = VAR == VAR_SPLIT;
     static constexpr bool VSTAGE = VAR == VAR_VGPR;
+    // SPREAD: the next entry's loads are issued a few per k-step, between the
+    // fragment reads and MFMAs, instead of all at the top of the iteration
+    static constexpr bool SPREAD = VAR == VAR_SPREAD;
     static constexpr int CPOL = VAR == VAR_NT ? 2 : (VAR == VAR_SC1 ? 16 : 0);
     static constexpr int RSL = SPLIT ? RS / 2 : RS;   // rows per load round of one loader
     static constexpr int HW = NT / 128;                // wavefronts per operand when split
@@ -315,20 +318,26 @@ struct RingTile {
         // re-read it into a stage that is free), so a fixed vmcnt tells which
         // entry has landed. The host sends problems with no full K tile
         // (KF == 0) to the generic kernel.
-        auto dma_entry = [&](int e) {
+        auto dma_one = [&](int e, int i) {   // load i of entry e
             int kt = e - NPRE;
             kt = kt < KF - 1 ? kt : KF - 1;
-            const uint8_t *a = Ab + (int64_t)kt * BKB;
-            const uint8_t *b = Bb + (int64_t)kt * BKB;
-            uint8_t *S = smem + (e % NS) * STAGE;
+            const uint8_t *src = (ld_is_a(i) ? Ab : Bb) + (int64_t)kt * BKB + off[i];
+            if constexpr (VSTAGE)
+                R[i] = *reinterpret_cast<const i32x4 *>(src);
+            else
+                dma16_cp<CPOL>(src, smem + (e % NS) * STAGE + ld_dst(i));
+        };
+        auto dma_entry = [&](int e) {
 #pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                const uint8_t *src = (ld_is_a(i) ? a : b) + off[i];
-                if constexpr (VSTAGE)
-                    R[i] = *reinterpret_cast<const i32x4 *>(src);
-                else
-                    dma16_cp<CPOL>(src, S + ld_dst(i));
-            }
+            for (int i = 0; i < NL; ++i)
+                dma_one(e, i);
+        };
+        // the loads of entry e that go with k-step `step` (SPREAD)
+        auto dma_step = [&](int e, int step) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                if (i * STEPS / NL == step)
+                    dma_one(e, i);
         };
         // VGPR-staged variant: the registers of entry e -> its stage
         auto stage_regs = [&](int e) {
@@ -390,12 +399,15 @@ struct RingTile {
             const uint8_t *S = smem + (e % NS) * STAGE;
             const uint8_t *Snext = smem + ((e + 1) % NS) * STAGE;
             __builtin_amdgcn_sched_barrier(0);
-            dma_entry(e + NS - 1);
+            if constexpr (!SPREAD)
+                dma_entry(e + NS - 1);
 #pragma unroll
             for (int step = 0; step < STEPS - 1; ++step) {
                 // one scheduling region per k-step: fragment reads of the next
                 // step and the MFMAs of this one (no back-to-back MFMAs on one
                 // accumulator across steps)
+                if constexpr (SPREAD)
+                    dma_step(e + NS - 1, step);
                 if (step % 2 == 0) {
                     read_frags<BM, BKB, TM, TN>(S, step + 1, wm0, wn0, lane, fa1, fb1);
                     mfma_step<P, TM, TN>(fa0, fb0, acc);
@@ -405,6 +417,8 @@ struct RingTile {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if constexpr (SPREAD)
+                dma_step(e + NS - 1, STEPS - 1);
             mfma_step<P, TM, TN, 0, KA>(fa1, fb1, acc);
             __builtin_amdgcn_sched_barrier(0);
             stage_regs(e + NS - 1);   // (VGPR-staged variant only) into the free stage
@@ -842,6 +856,7 @@ static const CfgShape kCfg[CFG_COUNT] = {
     {256, 256, 128, 1, "256x256_bk128_ring2_nt"},
     {256, 256, 128, 1, "256x256_bk128_ring2_sc1"},
     {256, 256, 128, 1, "256x256_bk128_ring2_vgpr_staged"},
+    {256, 256, 128, 1, "256x256_bk128_ring2_spread_loads"},
 };
 
 const char *tile_cfg_name(int cfg) {
@@ -986,6 +1001,7 @@ static hipError_t launch_prec(int cfg, const GemmProblem &p, const StreamKPlan &
     case CFG_256x256_NT: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_NT>(p, sk, ws, stream);
     case CFG_256x256_SC1: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_SC1>(p, sk, ws, stream);
     case CFG_256x256_VGPR: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_VGPR>(p, sk, ws, stream);
+    case CFG_256x256_SPREAD: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_SPREAD>(p, sk, ws, stream);
     default: return hipErrorInvalidValue;
     }
 }

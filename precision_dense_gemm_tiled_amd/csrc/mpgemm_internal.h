@@ -46,6 +46,7 @@ enum TileCfg {
     CFG_256x256_NT = 14,    // tile loads non-temporal (nt)
     CFG_256x256_SC1 = 15,   // tile loads at device scope (sc1)
     CFG_256x256_VGPR = 16,  // tile loads staged through VGPRs instead of direct-to-LDS
+    CFG_256x256_SPREAD = 17,// the next stage's loads issued a few per k-step instead of all at once
     CFG_COUNT
 };
 

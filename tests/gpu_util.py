@@ -7,7 +7,7 @@ import numpy as np
 # override): 0-11 the ring kernel's shapes, 12 the 256 x 256 ping-pong kernel,
 # 13-16 one-change ablations of the 256 x 256 ring (split loaders, nt, sc1,
 # VGPR-staged loads).
-N_TILE_CFGS = 17
+N_TILE_CFGS = 18
 PINGPONG_CFG = 12
 
 
