@@ -12,7 +12,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MPGEMM_ORACLE_LIB points the pins at another build of oracle.c (the
+# mutation test's deliberately broken copies); unset, the library built here.
+_LIB_PATH = os.environ.get("MPGEMM_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 OK, ERR_ARG, ERR_OVERFLOW = 0, 1, 2
