@@ -422,15 +422,24 @@ def test_w4a16_exact_small_integers(M, G):
     assert np.array_equal(_w4(X, W, S, G), oracle.f16_encode_rne_array(y))
 
 
-def test_w4a16_strided():
+@pytest.mark.parametrize("M,N,K,G,cfg", [(9, 40, 256, 128, None), (200, 100, 1440, 32, 12), (150, 70, 512, 64, 12),
+                                         (40, 72, 640, 128, 10)])
+def test_w4a16_strided(M, N, K, G, cfg, monkeypatch):
+    """Operands with padded rows (NaN activations and scales, 0x88 weights
+    past K) and an output with padded columns: nothing past K or N is read
+    into a result or written; for the default small-M kernel, the ring
+    kernel (ragged M, N and a partial last stage, K split over workgroups)
+    and the slice kernel."""
     import torch
-    M, N, K, G = 9, 40, 256, 128
-    X, W, S = inputs.w4a16_problem(M, N, K, G, seed=3)
+    if cfg is not None:
+        monkeypatch.setenv("MPGEMM_W4A16_CFG", str(cfg))
+    X, W, S = inputs.w4a16_problem(M, N, K, G, seed=3 + M)
     Xb = np.zeros((M, K + 64), np.float16); Xb[:, :K] = X; Xb[:, K:] = np.nan
     Wb = np.full((N, K // 2 + 32), 0x88, np.uint8); Wb[:, :K // 2] = W
     Sb = np.full((N, K // G + 5), np.nan, np.float16); Sb[:, :K // G] = S
     ybig = torch.full((M, N + 8), -7.0, dtype=torch.float16, device="cuda")
-    mp.gemm_w4a16(dev(Xb)[:, :K], dev(Wb)[:, :K // 2], dev(Sb)[:, :K // G], G, out=ybig[:, :N])
+    with mp.Handle() as h:
+        mp.gemm_w4a16(dev(Xb)[:, :K], dev(Wb)[:, :K // 2], dev(Sb)[:, :K // G], G, out=ybig[:, :N], handle=h.value)
     whole = host(ybig)
     y, t2 = oracle.gemm_w4a16(X, W, S, K, G, want_t2=True)
     assert np.all(np.abs(whole[:, :N].astype(np.float64) - y) <= w4a16_tol(y, t2, K))
