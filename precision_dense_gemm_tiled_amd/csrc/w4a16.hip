@@ -580,27 +580,40 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
 // Y = fp16(sum of the KS fp32 partial tiles), slices added in slice order.
 // Partial tile layout (as written by w4a16_slice_kernel): element
 // ((i * NB + j) * 4 + r) * (64 * WN) + t holds row 16 i + 4 ((t % 64) / 16) + r
-// and column (t / 64) * 16 NB + 16 j + t % 16 of the BM x BN tile.
+// and column (t / 64) * 16 NB + 16 j + t % 16 of the BM x BN tile. Four
+// consecutive elements (t % 4 == 0) are four consecutive columns of one row:
+// one thread adds them as a 16-byte vector per slice and stores 4 fp16.
 template <int MB, int NB, int WN>
 __global__ __launch_bounds__(256) void w4a16_reduce_kernel(W4A16Problem p, W4A16Split sk) {
     constexpr int BM = 16 * MB, BN = 16 * NB * WN, TILE = BM * BN;
+    static_assert(TILE % 4 == 0 && (64 * WN) % 4 == 0, "vector groups");
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t tiles = (int64_t)sk.mblocks * sk.ngroups;
-    if (e >= tiles * TILE)
+    if (e >= tiles * (TILE / 4))
         return;
-    const int tile = (int)(e / TILE), q = (int)(e % TILE);
+    const int tile = (int)(e / (TILE / 4)), q = 4 * (int)(e % (TILE / 4));
     const int t = q % (64 * WN), reg = q / (64 * WN);
     const int r = reg % 4, j = (reg / 4) % NB, i = reg / (4 * NB);
     const int lane = t % 64, wn = t / 64;
     const int mb = tile % sk.mblocks, ng = tile / sk.mblocks;
     const int m = mb * BM + 16 * i + 4 * (lane / 16) + r;
     const int n = ng * BN + wn * 16 * NB + 16 * j + lane % 16;
-    const float *src = sk.partial + (int64_t)tile * sk.ks * TILE + q;
-    float y = 0.f;
-    for (int o = 0; o < sk.ks; ++o)
-        y += src[(int64_t)o * TILE];
-    if (m < p.M && n < p.N)
-        p.Y[(int64_t)m * p.ldy + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(sk.partial + (int64_t)tile * sk.ks * TILE + q);
+    f32x4 y = src[0];
+    for (int o = 1; o < sk.ks; ++o)
+        y += src[(int64_t)o * (TILE / 4)];
+    if (m >= p.M)
+        return;
+    uint16_t *dst = p.Y + (int64_t)m * p.ldy + n;
+    if (n + 4 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<f16x4 *>(dst) = f16x4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (n + c < p.N)
+                dst[c] = __builtin_bit_cast(uint16_t, (_Float16)y[c]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1089,7 +1102,7 @@ static hipError_t launch_slice(const W4A16Problem &p, const W4A16Plan &plan, con
                        p, sk, lg);
     if (sk.ks == 1)
         return hipGetLastError();
-    const int64_t total = tiles * BM * BN;
+    const int64_t total = tiles * BM * BN / 4;   // one thread per 4 outputs
     hipLaunchKernelGGL((w4a16_reduce_kernel<MB, NB, WN>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                        stream, p, sk);
     return hipGetLastError();
