@@ -375,11 +375,11 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(W4A16Problem p, int lg)
 // fused-int4-gemm-sm75 README dequantises to fp16 in registers before the
 // matrix product).
 //
-// Dequantisation in natural k order, so the activations need no reordering:
-// with u = nibble ^ 8 = q + 8, broadcasting byte b of u to all four bytes puts
-// nibble 2b in bits 0..3 and nibble 2b+1 in bits 20..23; one mask-or with the
-// fp16 patterns 0x6400 (1024, unit step) and 0x5400 (64, step 1/16) gives the
-// pair (1024 + u_2b, 64 + u_2b+1), and subtracting (1032, 72) gives q exactly.
+// Dequantisation in natural k order, so the activations need no reordering
+// (dequant8_perm below): with u = nibble ^ 8 = q + 8, the fp16 patterns 0x6400
+// (1024, unit step) and 0x5400 (64, step 1/16) around nibbles 2b and 2b+1 give
+// the pair (1024 + u_2b, 64 + u_2b+1), and subtracting (1032, 72) gives q
+// exactly.
 //
 // The 4 wavefronts are arranged WN (columns) x WK (K quarters); the WK
 // partial sums meet in LDS. When the grid still has too few workgroups, K is
@@ -417,17 +417,6 @@ __device__ __forceinline__ int xcd_contiguous(int id, int nblk) {
     return xcd * base + (xcd < rem ? xcd : rem) + local;
 }
 
-__device__ __forceinline__ f16x8 dequant8_natural(uint32_t w, f16x2 s2) {
-    const uint32_t u = w ^ 0x88888888u;
-    const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-72.0f};
-    f16x2 q[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const uint32_t bb = __builtin_amdgcn_perm(u, u, 0x01010101u * (uint32_t)b);
-        q[b] = (__builtin_bit_cast(f16x2, (bb & 0x00F0000Fu) | 0x54006400u) + bias) * s2;
-    }
-    return f16x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
-}
 
 template <int MB, int NB, int WN, int WK, int NST>
 __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16Split sk, int lg) {
@@ -520,7 +509,7 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
                 // a run past the K range gets q = 0 (u = 8 in every nibble)
                 const uint32_t w = live ? (uint32_t)wr[s][j][t] : 0u;
                 const _Float16 sc = __builtin_bit_cast(_Float16, sr[s][j]);
-                const f16x8 b = dequant8_natural(w, f16x2{sc, sc});
+                const f16x8 b = dequant8_perm(w, f16x2{sc, sc});
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b, acc[i][j], 0, 0, 0);
