@@ -1202,9 +1202,11 @@ const char *w4a16_cfg_name(int cfg) {
 int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K) {
     (void)N;
     (void)K;
-    // measured at N = K = 4096 (cold weights, HIP graph replay): the ring
-    // kernel ties the 64 x 128 slices at M = 128 (19.6 vs 19.2 us) and wins
-    // from M = 192 on (22 vs 30 us; 29 vs 66 at 512, 82 vs 283 at 1024)
+    // measured at N = K = 4096 (cold weights, HIP graph replay): above 64
+    // rows the ring kernel wins (M = 80: 17.1 vs 18.5 us for the 64 x 128
+    // slices, M = 112: 18.1 vs 18.6; 29 vs 66 at 512, 54 vs 283 at 1024),
+    // except at M = 128, where the slices fill both their row blocks and the
+    // two tie (18.6 vs 18.7 us)
     if (M == 1)
         return W4A16_GEMV_R2_KS2;
     if (M <= 4)
@@ -1213,7 +1215,7 @@ int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K) {
         return W4A16_SLICE_16x16_K4;
     if (M <= 64)
         return W4A16_SLICE_32x32_K2;
-    if (M <= 128)
+    if (M == 128)
         return W4A16_SLICE_64x128;
     return W4A16_RING3_128x64;
 }

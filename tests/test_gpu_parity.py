@@ -346,13 +346,14 @@ def test_w4a16_ragged(M, N, K, G):
 W4A16_CFGS = 14
 
 
-@pytest.mark.parametrize("M,N,K,G", [(256, 4096, 4096, 128), (512, 4096, 4096, 128), (300, 200, 1440, 32),
-                                     (640, 2048, 8192, 256)])
+@pytest.mark.parametrize("M,N,K,G", [(96, 4096, 4096, 128), (256, 4096, 4096, 128), (512, 4096, 4096, 128),
+                                     (300, 200, 1440, 32), (640, 2048, 8192, 256)])
 def test_w4a16_prefill_sizes(M, N, K, G):
-    """Larger M runs the 128 x 64 ring kernel by default: K split over 2
-    workgroups (M = 256), no split (M = 512), ragged M with G = 32 and a
-    partial last stage (K = 1440), 32 stages per workgroup (K = 8192 in 2
-    slices); every element against the oracle."""
+    """M above 64 (but 128) runs the 128 x 64 ring kernel by default: K split
+    over 4 workgroups (M = 96, a partial row block) or 2 (M = 256), no split
+    (M = 512), ragged M with G = 32 and a partial last stage (K = 1440), 32
+    stages per workgroup (K = 8192 in 2 slices); every element against the
+    oracle."""
     X, W, S = inputs.w4a16_problem(M, N, K, G, seed=M + K + G)
     _check_w4(X, W, S, K, G, f"w4a16 {M}x{N}x{K} G={G}")
 
