@@ -475,6 +475,228 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(GemmProblem p
     RT::epilogue(p, smem, row0, col0, tid, lane, wave, acc);
 }
 
+// Direct-to-register variant of the 256 x 256 tile: A goes through the LDS
+// ring as in RingTile, B does not touch LDS. Each wavefront loads the B
+// fragments of its 128 columns straight from global memory into registers,
+// one stage ahead, in the MFMA operand layout (lane l holds column l % 32 of
+// a 32-column block). That halves the LDS traffic per MFMA (fragment reads
+// and DMA writes both carry A only) at the price of reading every B row from
+// L2 twice per workgroup (the two wavefronts of a column pair).
+//
+// K order inside a 128-byte stage: lane group g = l / 32 takes chunk 4g + s
+// at k-step s, so one lane's B bytes over the stage are 64 contiguous bytes
+// of its row. A's fragment reads use the same chunk, so both operands present
+// the same k to each MFMA product and the dot product is unchanged.
+//
+// Iteration e (stage e in LDS slot e % NS, B registers hold stage e): the
+// direct-to-LDS loads of A entry e + NS - 1 into the slot freed by entry
+// e - 1; per k-step s the A fragment reads of step s + 1, the MFMAs of step
+// s, then the B loads of step s of stage e + 1 into the registers those
+// MFMAs just consumed. Entries past the last K tile re-read it (unused), so
+// every iteration issues the same 8 + 16 loads and the wait for A entry
+// e + 1 is a constant vmcnt. K must be a whole number of stages.
+//
+// Measured on MI355X slower than the ring kernel it varies (INT8 8192^3:
+// 1630 vs 2205 TOP/s, FP16 859 vs 1185 TFLOP/s, INT4 2452 vs 2582 TOP/s),
+// with the same result for a 3-stage A ring: one B load instruction touches
+// 32 rows (the MFMA layout puts one row per lane), 32 cache lines for 1 KiB,
+// where a direct-to-LDS load touches 8, and the compute unit's load path,
+// not LDS, sets the pace. Kept as an ablation configuration
+// (CFG_256x256_DTV, built with NS = 2).
+// vmcnt wait that leaves lgkmcnt (LDS reads in flight) alone.
+template <int VM>
+__device__ __forceinline__ void wait_vm_only() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    constexpr int imm = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8);
+    __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// A 16-byte global load into a VGPR quad through inline assembly (uniform
+// 64-bit base in SGPRs, 32-bit lane offset), which the compiler does not
+// count: its analysis of loop-carried register loads falls back to waiting
+// for every load in flight, including the A tile just issued. The register
+// is tied in and out, so the load writes the quad that holds the variable;
+// the value may be read only after a wait that covers the load and
+// untracked_ready16().
+__device__ __forceinline__ void load16_untracked(i32x4 &v, uint32_t voff, const void *sbase) {
+    asm volatile("global_load_dwordx4 %0, %1, %2" : "+v"(v) : "v"(voff), "s"(sbase));
+}
+__device__ __forceinline__ void untracked_ready16(i32x4 &v) { asm volatile("" : "+v"(v)); }
+
+template <int P, int NS>
+struct DtvTile {
+    static constexpr int BM = 256, BN = 256, BKB = 128, WGM = 2, WGN = 2;
+    static constexpr int NT = 256, WTM = 128, WTN = 128, TM = 4, TN = 4;
+    static constexpr int CPR = BKB / 16, RS = NT / CPR, NLA = BM / RS;   // 8 A loads per thread
+    static constexpr int STEPS = CPR / 2;                                 // 4 k-steps per stage
+    static constexpr int NLB = STEPS * TN;                                // 16 B loads per lane
+    static constexpr int STAGE = BM * BKB;
+    static constexpr int LDS_BYTES = NS * STAGE;
+    // vmcnt when A entry e + 1 must have landed (end of iteration e): the B
+    // loads of steps 0..2 of this iteration, plus for NS = 3 everything issued
+    // since entry e + 1 at the top of iteration e - 1.
+    static constexpr int WAIT_A = 3 * TN + (NS - 2) * (NLA + NLB);
+    // vmcnt before the MFMAs of a k-step: its B registers were loaded one
+    // stage earlier; younger are the other three steps' B loads and this
+    // iteration's A loads.
+    static constexpr int WAIT_B = 3 * TN + NLA;
+    static_assert(NS == 2 || NS == 3, "vmcnt of the A wait must fit 6 bits");
+    static_assert(WAIT_A < 64 && 8 * (NS - 2) + NLB < 64, "vmcnt range");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
+    typedef typename AccOf<P>::type acc_t;
+
+    static __device__ __forceinline__ void read_a(const uint8_t *As, int step, int wm0, int lane,
+                                                  i32x4 (&a)[TM]) {
+        const int c = 4 * (lane >> 5) + step;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm0 + i * 32 + (lane & 31);
+            a[i] = *reinterpret_cast<const i32x4 *>(As + r * BKB + ((c ^ swz<CPR>(r)) * 16));
+        }
+    }
+
+    static __device__ __forceinline__ void mainloop(const GemmProblem &p, uint8_t *smem, int row0,
+                                                    int col0, int tid, int lane, int wave,
+                                                    acc_t (&acc)[TM][TN]) {
+        const int wm0 = (wave / WGN) * WTM;
+        const int wn0 = (wave % WGN) * WTN;
+        const int KT = (int)(p.kbytes / BKB);
+
+        // A: thread tid loads rows r0 + RS * i, chunk slot tid % CPR
+        const int r0 = tid / CPR;
+        const int cg = (tid % CPR) ^ swz<CPR>(r0);
+        const uint8_t *Ab = p.A + (int64_t)row0 * p.lda_b;
+        const int a_rows = p.M - row0;
+        uint32_t aoff[NLA];
+#pragma unroll
+        for (int i = 0; i < NLA; ++i) {
+            int r = r0 + i * RS;
+            r = r < a_rows ? r : a_rows - 1;   // clamped rows feed outputs never stored
+            aoff[i] = (uint32_t)r * (uint32_t)p.lda_b + cg * 16;
+        }
+        const int wrow = wave * (64 / CPR);
+        // B: lane l of block j reads row wn0 + 32 j + l % 32, bytes 64 (l / 32) ...
+        const uint8_t *Bb = p.B + (int64_t)col0 * p.ldb_b;
+        const int b_rows = p.N - col0;
+        uint32_t boff[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            int r = wn0 + j * 32 + (lane & 31);
+            r = r < b_rows ? r : b_rows - 1;
+            boff[j] = (uint32_t)r * (uint32_t)p.ldb_b + 64 * (lane >> 5);
+        }
+
+        auto dma_a = [&](int e) {
+            const int kt = e < KT - 1 ? e : KT - 1;
+            uint8_t *S = smem + (e % NS) * STAGE;
+#pragma unroll
+            for (int i = 0; i < NLA; ++i)
+                dma16_cp<0>(Ab + (int64_t)kt * BKB + aoff[i], S + (wrow + i * RS) * BKB);
+        };
+        // B registers of the current stage; load_b(e, s) refills breg[s] with
+        // step s of stage e. The loads are untracked (see load16_untracked),
+        // so the consumers wait with wait_vm_only<WAIT_B>() and b_ready().
+        i32x4 breg[STEPS][TN];
+        auto load_b = [&](int e, int s) {
+            const int kt = e < KT - 1 ? e : KT - 1;
+            const uint8_t *src = Bb + (int64_t)kt * BKB + 16 * s;   // uniform
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                load16_untracked(breg[s][j], boff[j], src);
+        };
+        auto b_ready = [&](int s) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                untracked_ready16(breg[s][j]);
+        };
+
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = acc_t{};
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                breg[s][j] = i32x4{0, 0, 0, 0};
+
+        i32x4 fa0[TM], fa1[TM];
+#pragma unroll
+        for (int e = 0; e < NS - 1; ++e)
+            dma_a(e);
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s)
+            load_b(0, s);
+        wait_vm_lds<NLA * (NS - 2) + NLB>();   // A entry 0
+        lds_barrier();
+        read_a(smem, 0, wm0, lane, fa0);
+
+        constexpr int NMF = TM * TN;
+        constexpr int KA = NMF / 4;
+        for (int e = 0; e < KT; ++e) {
+            const uint8_t *S = smem + (e % NS) * STAGE;
+            const uint8_t *Snext = smem + ((e + 1) % NS) * STAGE;
+            __builtin_amdgcn_sched_barrier(0);
+            dma_a(e + NS - 1);
+#pragma unroll
+            for (int step = 0; step < STEPS - 1; ++step) {
+                if (step % 2 == 0)
+                    read_a(S, step + 1, wm0, lane, fa1);
+                else
+                    read_a(S, step + 1, wm0, lane, fa0);
+                wait_vm_only<WAIT_B>();
+                b_ready(step);
+                if (step % 2 == 0)
+                    mfma_step<P, TM, TN>(fa0, breg[step], acc);
+                else
+                    mfma_step<P, TM, TN>(fa1, breg[step], acc);
+                load_b(e + 1, step);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_vm_only<WAIT_B>();
+            b_ready(STEPS - 1);
+            mfma_step<P, TM, TN, 0, KA>(fa1, breg[STEPS - 1], acc);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm_lds<WAIT_A>();
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            read_a(Snext, 0, wm0, lane, fa0);
+            mfma_step<P, TM, TN, KA, NMF>(fa1, breg[STEPS - 1], acc);
+            load_b(e + 1, STEPS - 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // The last entries' dummy loads must land before the ring is reused,
+        // and the last B loads before their registers are: the registers stay
+        // live up to here, so the compiler cannot hand them to the epilogue
+        // while those loads are still in flight.
+        wait_vm_lds<0>();
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s)
+            b_ready(s);
+    }
+};
+
+// Data-parallel kernel of DtvTile (K a whole number of 128-byte stages).
+template <int P, int NS>
+__global__ __launch_bounds__(256) void gemm_dtv_kernel(GemmProblem p, int tiles_m, int tiles_n) {
+    typedef DtvTile<P, NS> DT;
+    typedef RingTile<P, 256, 256, 128, 2, 2, 2> RT;   // same wavefront tiles: its epilogue
+    static_assert(RT::LDS_BYTES >= (256 + 2 * 256) * 4, "epilogue staging");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[DT::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int row0 = tm * 256, col0 = tn * 256;
+
+    typename DT::acc_t acc[DT::TM][DT::TN];
+    DT::mainloop(p, smem, row0, col0, tid, lane, wave, acc);
+    RT::epilogue(p, smem, row0, col0, tid, lane, wave, acc);
+}
+
 // Ping-pong kernel for the 256 x 256 tile (data-parallel, K a multiple of
 // the 128-byte stage, at least two stages). Eight wavefronts, two per SIMD,
 // in two groups of four (wavefronts q and q + 4 share SIMD q) that run the
@@ -857,6 +1079,7 @@ static const CfgShape kCfg[CFG_COUNT] = {
     {256, 256, 128, 1, "256x256_bk128_ring2_sc1"},
     {256, 256, 128, 1, "256x256_bk128_ring2_vgpr_staged"},
     {256, 256, 128, 1, "256x256_bk128_ring2_spread_loads"},
+    {256, 256, 128, 1, "256x256_bk128_a_ring2_b_direct"},
 };
 
 const char *tile_cfg_name(int cfg) {
@@ -962,6 +1185,19 @@ static hipError_t launch_pp(const GemmProblem &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// B-direct kernel: data-parallel launches with K a whole number of stages;
+// anything else goes to the ring kernel of the same tile shape.
+template <int P, int NS>
+static hipError_t launch_dtv(const GemmProblem &p, const StreamKPlan &sk, const TileWorkspace &ws,
+                             hipStream_t stream) {
+    if (sk.grid > 0 || p.kbytes % 128 != 0 || p.kbytes < 128)
+        return launch_one<P, 256, 256, 128, 2, 2, 2>(p, sk, ws, stream);
+    const int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
+    hipLaunchKernelGGL((gemm_dtv_kernel<P, NS>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, p,
+                       tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 template <int P>
 static hipError_t launch_generic(const GemmProblem &p, hipStream_t stream) {
     constexpr int BM = 128, BN = 128;
@@ -1002,6 +1238,7 @@ static hipError_t launch_prec(int cfg, const GemmProblem &p, const StreamKPlan &
     case CFG_256x256_SC1: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_SC1>(p, sk, ws, stream);
     case CFG_256x256_VGPR: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_VGPR>(p, sk, ws, stream);
     case CFG_256x256_SPREAD: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_SPREAD>(p, sk, ws, stream);
+    case CFG_256x256_DTV: return launch_dtv<P, 2>(p, sk, ws, stream);
     default: return hipErrorInvalidValue;
     }
 }

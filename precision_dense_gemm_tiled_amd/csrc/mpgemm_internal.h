@@ -47,6 +47,7 @@ enum TileCfg {
     CFG_256x256_SC1 = 15,   // tile loads at device scope (sc1)
     CFG_256x256_VGPR = 16,  // tile loads staged through VGPRs instead of direct-to-LDS
     CFG_256x256_SPREAD = 17,// the next stage's loads issued a few per k-step instead of all at once
+    CFG_256x256_DTV = 18,   // B straight from global memory into MFMA registers, only A through LDS
     CFG_COUNT
 };
 

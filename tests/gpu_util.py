@@ -5,10 +5,12 @@ import numpy as np
 
 # Tile configurations of the GEMM kernels (indices of the MPGEMM_TILE_CFG
 # override): 0-11 the ring kernel's shapes, 12 the 256 x 256 ping-pong kernel,
-# 13-16 one-change ablations of the 256 x 256 ring (split loaders, nt, sc1,
-# VGPR-staged loads).
-N_TILE_CFGS = 18
+# 13-17 one-change ablations of the 256 x 256 ring (split loaders, nt, sc1,
+# VGPR-staged loads, spread loads), 18 the 256 x 256 kernel with B loaded
+# straight into registers.
+N_TILE_CFGS = 19
 PINGPONG_CFG = 12
+B_DIRECT_CFGS = (18,)
 
 
 def require_gpu():

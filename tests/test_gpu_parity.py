@@ -12,7 +12,7 @@ import pytest
 import oracle
 import precision_dense_gemm_tiled_amd as mp
 from precision_dense_gemm_tiled_amd import inputs
-from tests.gpu_util import (N_TILE_CFGS, PINGPONG_CFG, dev, f16_tol, freivalds_int, host, pack_i4,
+from tests.gpu_util import (B_DIRECT_CFGS, N_TILE_CFGS, PINGPONG_CFG, dev, f16_tol, freivalds_int, host, pack_i4,
                             require_gpu, sample_rows, unpack_i4, w4a16_tol)
 
 pytestmark = pytest.mark.gpu
@@ -82,20 +82,24 @@ def test_every_tile_config(prec, monkeypatch):
         _compare(prec, got, ref, K, f"{prec} cfg {cfg}")
 
 
-# (M, N, K bytes per row): the ping-pong kernel needs K in whole 128-byte
-# stages, at least two; ragged M and N tiles, a single output, one tile, a
-# grid of several tiles with a longer K.
+# (M, N, K bytes per row): the ping-pong and B-direct kernels need K in whole
+# 128-byte stages (ping-pong: at least two); ragged M and N tiles, a single
+# output, one tile, a grid of several tiles with a longer K.
 PINGPONG_SHAPES = [(300, 520, 256), (513, 260, 1024), (1, 1, 256), (256, 256, 384), (700, 1000, 2048)]
+WHOLE_STAGE_CASES = ([(PINGPONG_CFG, *s) for s in PINGPONG_SHAPES] +
+                     [(c, *s) for c in B_DIRECT_CFGS for s in PINGPONG_SHAPES + [(260, 300, 128)]])
 
 
 @pytest.mark.parametrize("prec", ["i8", "i4", "f16"])
-@pytest.mark.parametrize("M,N,kb", PINGPONG_SHAPES)
-def test_pingpong_config(prec, M, N, kb, monkeypatch):
-    """The 256 x 256 ping-pong kernel (forced) against the oracle, and a
-    second call on the same inputs bit-identical to the first."""
+@pytest.mark.parametrize("cfg,M,N,kb", WHOLE_STAGE_CASES)
+def test_whole_stage_config(prec, cfg, M, N, kb, monkeypatch):
+    """The kernels that run only on K in whole 128-byte stages (the 256 x 256
+    ping-pong kernel, the kernels that load B straight into registers),
+    forced, against the oracle, and a second call on the same inputs
+    bit-identical to the first."""
     K = {"i8": kb, "f16": kb // 2, "i4": 2 * kb}[prec]
     A, B = inputs.gemm_problem(prec, M, N, K, seed=1000 + M + N + kb)
-    monkeypatch.setenv("MPGEMM_TILE_CFG", str(PINGPONG_CFG))
+    monkeypatch.setenv("MPGEMM_TILE_CFG", str(cfg))
     with mp.Handle() as h:
         a, b = dev(A), dev(B)
         runs = []
@@ -106,7 +110,7 @@ def test_pingpong_config(prec, M, N, kb, monkeypatch):
                 runs.append(host(mp.gemm_i4(a, b, K, handle=h.value)))
             else:
                 runs.append(host(mp.gemm_f16(a, b, handle=h.value)))
-    _compare(prec, runs[0], _ref(prec, A, B, K), K, f"{prec} ping-pong {M}x{N}x{K}")
+    _compare(prec, runs[0], _ref(prec, A, B, K), K, f"{prec} cfg {cfg} {M}x{N}x{K}")
     assert np.array_equal(runs[0].view(np.uint32), runs[1].view(np.uint32)), "repeat differs"
 
 
@@ -474,9 +478,12 @@ def test_w4a4_against_oracle(M, N, K, with_bias):
     _w4a4_check(A, B, K, sx, sw, b, got, f"w4a4 {M}x{N}x{K}")
 
 
-def test_w4a4_every_tile_config(monkeypatch):
-    M, N, K = 300, 520, 200
-    A, B, sx, sw, b = inputs.w4a4_problem(M, N, K, seed=78)
+@pytest.mark.parametrize("K", [200, 512])
+def test_w4a4_every_tile_config(K, monkeypatch):
+    """Every tile configuration with the scale epilogue; K = 512 (256 bytes
+    per row) also reaches the kernels that need whole 128-byte stages."""
+    M, N = 300, 520
+    A, B, sx, sw, b = inputs.w4a4_problem(M, N, K, seed=78 + K)
     for cfg in range(N_TILE_CFGS):
         monkeypatch.setenv("MPGEMM_TILE_CFG", str(cfg))
         with mp.Handle() as h:
