@@ -123,10 +123,11 @@ class Problem:
     """Device-resident inputs of one (precision, shape), with `copies` distinct
     input sets when the working set would otherwise stay in the MALL."""
 
-    def __init__(self, prec, M, N, K, seed, copies=1):
+    def __init__(self, prec, M, N, K, seed, copies=1, b_layout="nk"):
         import torch
         from precision_dense_gemm_tiled_amd import inputs
         self.prec, self.M, self.N, self.K = prec, M, N, K
+        self.b_layout = b_layout
         if prec == "w4a4":
             A, B, SX, SW, BI = inputs.w4a4_problem(M, N, K, seed)
             t = [torch.from_numpy(v).cuda() for v in (A, B, SX, SW, BI)]
@@ -145,6 +146,8 @@ class Problem:
             self.out = torch.empty((M, N), dtype=torch.float16, device="cuda")
         else:
             A, B = inputs.gemm_problem(prec, M, N, K, seed)
+            if b_layout == "kn":
+                B = transpose_b(prec, B, N, K)
             a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
             self.ins = [(a, b)] + [(a.clone(), b.clone()) for _ in range(copies - 1)]
             odt = torch.float32 if prec == "f16" else torch.int32
@@ -155,7 +158,12 @@ class Problem:
         import precision_dense_gemm_tiled_amd as mp
         ins = self.ins[self.i % len(self.ins)]
         self.i += 1
-        if self.prec == "f16":
+        if self.b_layout == "kn":
+            if self.prec == "i4":
+                mp.gemm_i4_kn(ins[0], ins[1], self.N, out=self.out)
+            else:
+                (mp.gemm_f16_kn if self.prec == "f16" else mp.gemm_i8_kn)(ins[0], ins[1], out=self.out)
+        elif self.prec == "f16":
             mp.gemm_f16(ins[0], ins[1], out=self.out)
         elif self.prec == "i8":
             mp.gemm_i8(ins[0], ins[1], out=self.out)
@@ -167,6 +175,23 @@ class Problem:
             mp.gemm_w4a4(ins[0], ins[1], self.K, ins[2], ins[3], ins[4], out=self.out)
         else:
             mp.gemm_w4a16(ins[0], ins[1], ins[2], W4A16_G, out=self.out)
+
+
+def transpose_b(prec, B, N, K):
+    """B (N x K, packed along K for INT4) -> the same values stored K x N
+    (INT4: packed two n per byte, low nibble = even n), for the transposed-B
+    control. Host-side layout change only."""
+    import numpy as np
+    if prec != "i4":
+        return np.ascontiguousarray(B.T)
+    lo = (B & 0x0F).astype(np.uint8)
+    hi = (B >> 4).astype(np.uint8)
+    q = np.empty((N, 2 * B.shape[1]), dtype=np.uint8)   # nibbles, N x K
+    q[:, 0::2], q[:, 1::2] = lo, hi
+    qt = np.ascontiguousarray(q[:, :K].T)               # K x N
+    if N % 2:
+        qt = np.concatenate([qt, np.zeros((K, 1), dtype=np.uint8)], axis=1)
+    return (qt[:, 0::2] | (qt[:, 1::2] << 4)).astype(np.uint8)
 
 
 def copies_for_cold(prec, M, N, K):
@@ -230,9 +255,9 @@ def time_graph(prob, launches, replays):
     return start.elapsed_time(stop) / 1e3 / (replays * launches)
 
 
-def sweep_entry(prec, M, N, K, seed, steps, warmup, eager=False):
+def sweep_entry(prec, M, N, K, seed, steps, warmup, eager=False, b_layout="nk"):
     copies = copies_for_cold(prec, M, N, K)
-    p = Problem(prec, M, N, K, seed, copies)
+    p = Problem(prec, M, N, K, seed, copies, b_layout)
     # expected kernel time at ~30% of the roofline sets the launches per graph
     est_s = max(roofline(prec, M, N, K, 1.0)["ops"] / (PEAK.get(prec, 2500.0) * 1e12 * 0.3),
                 algorithmic_bytes(prec, M, N, K) / (HBM_GBS * 1e9 * 0.3))
@@ -254,7 +279,7 @@ def sweep_entry(prec, M, N, K, seed, steps, warmup, eager=False):
     # Infinity Cache (reported beside the cold figure, never instead of it)
     t_warm = None
     if copies > 1 and not eager:
-        pw = Problem(prec, M, N, K, seed, 1)
+        pw = Problem(prec, M, N, K, seed, 1, b_layout)
         t_warm = time_graph(pw, launches, max(steps, 3))
         del pw
         torch.cuda.empty_cache()
@@ -268,6 +293,8 @@ def sweep_entry(prec, M, N, K, seed, steps, warmup, eager=False):
          "hbm_GBps_algorithmic": round(algorithmic_bytes(prec, M, N, K) / t / 1e9, 1),
          "input_copies": copies, "launches": reps,
          "timing": "eager launches" if eager else "hip graph replay"}
+    if b_layout != "nk":
+        e["b_layout"] = b_layout
     if t_warm is not None:
         e["us_warm"] = round(t_warm * 1e6, 3)
     return e
@@ -325,6 +352,9 @@ def main():
                     help="time only this precision's sweep (no headline line)")
     ap.add_argument("--sizes", type=str, default=None,
                     help="with --only: comma-separated sizes (N, or M for w4a16)")
+    ap.add_argument("--b-layout", choices=["nk", "kn"], default="nk",
+                    help="with --only f16/i8/i4: B stored N x K (default) or K x N (the "
+                         "transposed-B control, mpgemm_run_*_kn)")
     ap.add_argument("--eager", action="store_true",
                     help="time the sweep with eager launches instead of HIP graph replay")
     ap.add_argument("--calib-copy", action="store_true",
@@ -365,7 +395,8 @@ def main():
             for s in sizes:
                 M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else ((1, s, s) if prec == "quantize" else (s, s, s))
                 seed = inputs.config_seed(CONFIG_INDEX[prec], s)
-                e = sweep_entry(prec, M, N, K, seed, args.steps, args.warmup, args.eager)
+                layout = args.b_layout if prec in ("f16", "i8", "i4") else "nk"
+                e = sweep_entry(prec, M, N, K, seed, args.steps, args.warmup, args.eager, layout)
                 log(prec, e)
                 out[prec].append(e)
         print(json.dumps(out))

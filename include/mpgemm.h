@@ -12,6 +12,8 @@
  *                     fp16 scales, fp32 accumulate, fp16 Y
  *   mpgemm_run_w4a4   int4 x int4 with per-row and per-column fp16 scales and
  *                     a column bias applied to the exact int32 sum, fp16 Y
+ *   mpgemm_run_{f16,i8,i4}_kn  the first three with B stored K x N (the
+ *                     transposed layout, kept as a measured control)
  *
  * Sources: "Hand-Written PTX Tensor-Core GEMM Kernels: A Multi-Precision Study
  * on NVIDIA L4" (abstract and summary: the FP16 / INT8 / INT4 GEMM problem over
@@ -120,6 +122,31 @@ mpgemm_status_t mpgemm_run_i4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K
                               const uint8_t *A, int64_t lda,
                               const uint8_t *B, int64_t ldb,
                               int32_t *C, int64_t ldc, void *stream);
+
+/* Transposed-B layout: the control of the [L4 study] summary's ablation of
+ * the B operand's layout (the INT4 k64 paragraph: a transposed B is the
+ * worse layout). The same products as mpgemm_run_{f16,i8,i4}, with B stored
+ * K x N: C[m][n] = sum_k A[m][k] * Bt[k][n], Bt row-major with row stride
+ * ldbt >= N elements. A is M x K as above. For INT4 the elements of a Bt row
+ * are packed two per byte along n (byte n/2 of row k holds n in its low
+ * nibble when n is even); K, lda and ldbt must be even; N may be odd (the
+ * high nibble of a row's last byte is then ignored).
+ * These calls exist to measure that layout and have one kernel only: A and Bt
+ * must be 16-byte aligned with row strides that are multiples of 16 bytes,
+ * else MPGEMM_ERR_UNSUPPORTED. Everything else (ownership, errors, no-ops, K
+ * bound for the integer paths, accumulation) is as for the N x K calls. */
+mpgemm_status_t mpgemm_run_f16_kn(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                  const uint16_t *A, int64_t lda,
+                                  const uint16_t *Bt, int64_t ldbt,
+                                  float *C, int64_t ldc, void *stream);
+mpgemm_status_t mpgemm_run_i8_kn(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                 const int8_t *A, int64_t lda,
+                                 const int8_t *Bt, int64_t ldbt,
+                                 int32_t *C, int64_t ldc, void *stream);
+mpgemm_status_t mpgemm_run_i4_kn(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                 const uint8_t *A, int64_t lda,
+                                 const uint8_t *Bt, int64_t ldbt,
+                                 int32_t *C, int64_t ldc, void *stream);
 
 /* INT4 x INT4 GEMM with a scale epilogue ("Warp-Specialized Kernel
  * Implementation for W4A4 MatMul on Latest GPU Architectures", section 1:

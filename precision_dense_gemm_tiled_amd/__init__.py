@@ -14,8 +14,10 @@ __all__ = [
     "MpgemmError", "lib", "lib_path",
     "mpgemm_create", "mpgemm_destroy", "mpgemm_status_string",
     "mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_run_w4a4", "mpgemm_quantize_w4",
+    "mpgemm_run_f16_kn", "mpgemm_run_i8_kn", "mpgemm_run_i4_kn",
     "mpgemm_plan_gemm", "mpgemm_plan_w4a16",
     "Handle", "default_handle", "gemm_f16", "gemm_i8", "gemm_i4", "gemm_w4a16", "gemm_w4a4", "quantize_w4",
+    "gemm_f16_kn", "gemm_i8_kn", "gemm_i4_kn",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,7 +57,8 @@ def lib() -> ctypes.CDLL:
         L.mpgemm_destroy.restype = ctypes.c_int
         L.mpgemm_status_string.argtypes = [ctypes.c_int]
         L.mpgemm_status_string.restype = ctypes.c_char_p
-        for name in ("mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4"):
+        for name in ("mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4",
+                     "mpgemm_run_f16_kn", "mpgemm_run_i8_kn", "mpgemm_run_i4_kn"):
             f = getattr(L, name)
             f.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
             f.restype = ctypes.c_int
@@ -105,6 +108,18 @@ def mpgemm_run_i8(h, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
 
 def mpgemm_run_i4(h, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     return lib().mpgemm_run_i4(h, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def mpgemm_run_f16_kn(h, M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None) -> int:
+    return lib().mpgemm_run_f16_kn(h, M, N, K, A, lda, Bt, ldbt, C, ldc, stream)
+
+
+def mpgemm_run_i8_kn(h, M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None) -> int:
+    return lib().mpgemm_run_i8_kn(h, M, N, K, A, lda, Bt, ldbt, C, ldc, stream)
+
+
+def mpgemm_run_i4_kn(h, M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None) -> int:
+    return lib().mpgemm_run_i4_kn(h, M, N, K, A, lda, Bt, ldbt, C, ldc, stream)
 
 
 def mpgemm_run_w4a16(h, M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, stream=None) -> int:
@@ -227,6 +242,56 @@ def gemm_i8(A, B, out=None, handle=None, stream=None):
     h = default_handle(A.device.index) if handle is None else handle
     _check(mpgemm_run_i8(h, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
                          _stream(stream)), "mpgemm_run_i8")
+    return C
+
+
+def gemm_f16_kn(A, Bt, out=None, handle=None, stream=None):
+    """C = A @ Bt with fp16 A (M x K), Bt (K x N, the transposed-B layout)
+    -> fp32 C (M x N)."""
+    import torch
+    lda, ldbt = _rows(A, torch.float16, "A"), _rows(Bt, torch.float16, "Bt")
+    M, K = A.shape
+    if Bt.shape[0] != K:
+        raise ValueError("A and Bt disagree on K")
+    N = Bt.shape[1]
+    C = torch.empty((M, N), dtype=torch.float32, device=A.device) if out is None else out
+    ldc = _rows(C, torch.float32, "C")
+    h = default_handle(A.device.index) if handle is None else handle
+    _check(mpgemm_run_f16_kn(h, M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldbt, C.data_ptr(), ldc,
+                             _stream(stream)), "mpgemm_run_f16_kn")
+    return C
+
+
+def gemm_i8_kn(A, Bt, out=None, handle=None, stream=None):
+    """C = A @ Bt with int8 A (M x K), Bt (K x N) -> int32 C (M x N), exact."""
+    import torch
+    lda, ldbt = _rows(A, torch.int8, "A"), _rows(Bt, torch.int8, "Bt")
+    M, K = A.shape
+    if Bt.shape[0] != K:
+        raise ValueError("A and Bt disagree on K")
+    N = Bt.shape[1]
+    C = torch.empty((M, N), dtype=torch.int32, device=A.device) if out is None else out
+    ldc = _rows(C, torch.int32, "C")
+    h = default_handle(A.device.index) if handle is None else handle
+    _check(mpgemm_run_i8_kn(h, M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldbt, C.data_ptr(), ldc,
+                            _stream(stream)), "mpgemm_run_i8_kn")
+    return C
+
+
+def gemm_i4_kn(A, Bt, N, out=None, handle=None, stream=None):
+    """C = A @ Bt for signed INT4: A (M x K nibbles packed along K, uint8),
+    Bt (K x N nibbles packed two per byte along n, low nibble = even n) ->
+    int32 C (M x N), exact."""
+    import torch
+    lda_b, ldbt_b = _rows(A, torch.uint8, "A"), _rows(Bt, torch.uint8, "Bt")
+    M, K = A.shape[0], Bt.shape[0]
+    if 2 * Bt.shape[1] < N or 2 * A.shape[1] < K:
+        raise ValueError("packed rows shorter than N or K")
+    C = torch.empty((M, N), dtype=torch.int32, device=A.device) if out is None else out
+    ldc = _rows(C, torch.int32, "C")
+    h = default_handle(A.device.index) if handle is None else handle
+    _check(mpgemm_run_i4_kn(h, M, N, K, A.data_ptr(), 2 * lda_b, Bt.data_ptr(), 2 * ldbt_b, C.data_ptr(),
+                            ldc, _stream(stream)), "mpgemm_run_i4_kn")
     return C
 
 

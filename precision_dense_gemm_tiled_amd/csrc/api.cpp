@@ -128,6 +128,59 @@ mpgemm_status_t run_tile(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int6
     return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
 }
 
+// Checks of a transposed-B call: B^T is K x N (row stride ldbt elements).
+// That kernel has no byte-gather variant, so A and B^T rows must be 16-byte
+// aligned. The handle is checked last, as for the other calls.
+mpgemm_status_t check_gemm_kn(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K, const void *A,
+                              int64_t lda, const void *Bt, int64_t ldbt, const void *C, int64_t ldc,
+                              int elem_num, int elem_den, int out_bytes, int64_t max_k, bool *noop) {
+    *noop = false;
+    if (M < 0 || N < 0 || K < 0)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return MPGEMM_OK;
+    }
+    if (!C || (K > 0 && (!A || !Bt)))
+        return MPGEMM_ERR_INVALID_ARG;
+    if (lda < K || ldbt < N || ldc < N)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (M > INT_MAX || N > INT_MAX || K > max_k || lda > INT64_MAX / 4 || ldbt > INT64_MAX / 4)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if (((M + 255) / 256) * ((N + 255) / 256) > INT_MAX)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if ((lda * elem_num) % elem_den != 0 || (ldbt * elem_num) % elem_den != 0)
+        return MPGEMM_ERR_UNSUPPORTED;
+    // (K == 0 reads no operand: it writes zeros whatever the layout)
+    if (K > 0 && ((lda * elem_num / elem_den) % 16 != 0 || (ldbt * elem_num / elem_den) % 16 != 0 ||
+                  !aligned16(A) || !aligned16(Bt)))
+        return MPGEMM_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(C) % out_bytes) != 0)
+        return MPGEMM_ERR_UNSUPPORTED;
+    return h ? MPGEMM_OK : MPGEMM_ERR_INVALID_ARG;
+}
+
+mpgemm_status_t run_kn(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int64_t kbytes,
+                       const void *A, int64_t lda_b, const void *Bt, int64_t ldbt_b, void *C,
+                       int64_t ldc, void *stream) {
+    DeviceGuard dg(h->device);
+    if (!dg.ok)
+        return MPGEMM_ERR_HIP;
+    mpg::GemmProblem p;
+    p.A = static_cast<const uint8_t *>(A);
+    p.B = static_cast<const uint8_t *>(Bt);
+    p.C = C;
+    p.lda_b = lda_b;
+    p.ldb_b = ldbt_b;
+    p.ldc = ldc;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.kbytes = kbytes;
+    p.sx = p.sw = p.bias = nullptr;
+    hipError_t e = mpg::launch_gemm_kn(prec, p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -260,6 +313,41 @@ mpgemm_status_t mpgemm_run_i4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K
     if (st != MPGEMM_OK || noop)
         return st;
     return run_tile(h, mpg::PREC_I4, M, N, K / 2, A, lda / 2, B, ldb / 2, C, ldc, stream);
+}
+
+mpgemm_status_t mpgemm_run_f16_kn(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                  const uint16_t *A, int64_t lda, const uint16_t *Bt, int64_t ldbt,
+                                  float *C, int64_t ldc, void *stream) {
+    bool noop;
+    mpgemm_status_t st =
+        check_gemm_kn(h, M, N, K, A, lda, Bt, ldbt, C, ldc, 2, 1, 4, INT64_MAX / 4, &noop);
+    if (st != MPGEMM_OK || noop)
+        return st;
+    return run_kn(h, mpg::PREC_F16, M, N, 2 * K, A, 2 * lda, Bt, 2 * ldbt, C, ldc, stream);
+}
+
+mpgemm_status_t mpgemm_run_i8_kn(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                 const int8_t *A, int64_t lda, const int8_t *Bt, int64_t ldbt,
+                                 int32_t *C, int64_t ldc, void *stream) {
+    bool noop;
+    mpgemm_status_t st =
+        check_gemm_kn(h, M, N, K, A, lda, Bt, ldbt, C, ldc, 1, 1, 4, MPGEMM_MAX_K_INT, &noop);
+    if (st != MPGEMM_OK || noop)
+        return st;
+    return run_kn(h, mpg::PREC_I8, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
+}
+
+mpgemm_status_t mpgemm_run_i4_kn(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                 const uint8_t *A, int64_t lda, const uint8_t *Bt, int64_t ldbt,
+                                 int32_t *C, int64_t ldc, void *stream) {
+    if (M > 0 && N > 0 && K >= 0 && ((K % 2) != 0 || (lda % 2) != 0 || (ldbt % 2) != 0))
+        return MPGEMM_ERR_UNSUPPORTED;
+    bool noop;
+    mpgemm_status_t st =
+        check_gemm_kn(h, M, N, K, A, lda, Bt, ldbt, C, ldc, 1, 2, 4, MPGEMM_MAX_K_INT, &noop);
+    if (st != MPGEMM_OK || noop)
+        return st;
+    return run_kn(h, mpg::PREC_I4, M, N, K / 2, A, lda / 2, Bt, ldbt / 2, C, ldc, stream);
 }
 
 mpgemm_status_t mpgemm_run_w4a4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,

@@ -1055,6 +1055,131 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_generic_kernel(GemmP
     }
 }
 
+// Transposed-B control (the L4 study's ablation of the B operand's layout):
+// B is stored K x N, each row of B^T holding the N values of one k. For
+// INT4 two n share a byte (the low nibble holds the even n), since n is the
+// contiguous dimension. The kernel is the VGPR-staged two-buffer tile
+// kernel (as gemm_tile_generic_kernel, 16-byte aligned rows) with one change:
+// B's 16-byte chunks, coalesced along n, are written into the same
+// [n][k]-ordered, swizzled LDS layout as the N x K path, element by element
+// (INT4: a byte from the nibbles of two rows), so the fragment reads, the
+// MFMAs and the epilogue are unchanged. The transposition costs one LDS
+// write per element instead of one per 16 bytes.
+template <int P>
+__global__ __launch_bounds__(256) void gemm_tile_kn_kernel(GemmProblem p, int tiles_m, int tiles_n) {
+    constexpr int BM = 256, BN = 256, BKB = 128, WGN = 2;
+    constexpr int NT = 256, WTM = 128, WTN = 128, TM = 4, TN = 4;
+    constexpr int CPR = BKB / 16, RS = NT / CPR, A_PER_T = BM / RS;
+    constexpr int STAGE = (BM + BN) * BKB;
+    // B^T staging: chunks of 16 bytes along n. CPB chunks per B^T row of the
+    // tile; INT4 loads the chunks of rows 2 kp and 2 kp + 1 together.
+    constexpr int CPB = P == PREC_F16 ? 32 : (P == PREC_I8 ? 16 : 8);
+    constexpr int NPC = P == PREC_F16 ? 8 : (P == PREC_I8 ? 16 : 32);   // n per chunk
+    constexpr int ROWS = P == PREC_I4 ? 2 : 1;                          // B^T rows per item
+    constexpr int KPS = P == PREC_F16 ? 64 : (P == PREC_I8 ? 128 : 256);    // k per stage
+    constexpr int ITEMS = KPS / ROWS * CPB / NT;
+    static_assert(P != PREC_W4A4, "no scale epilogue on this path");
+    static_assert(ITEMS * ROWS == 8, "8 B chunks per thread per stage");
+    typedef typename AccOf<P>::type acc_t;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / WGN) * WTM, wn0 = (wave % WGN) * WTN;
+    int tm, tn;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int row0 = tm * BM, col0 = tn * BN;
+    const int64_t kbytes = p.kbytes;
+    // k values (INT4: nibbles) per row of A, and the bytes of one B^T row
+    const int64_t K = P == PREC_F16 ? kbytes / 2 : (P == PREC_I8 ? kbytes : 2 * kbytes);
+    const int64_t nbytes = P == PREC_F16 ? 2 * (int64_t)p.N : (P == PREC_I8 ? p.N : ((int64_t)p.N + 1) / 2);
+    const int KT = (int)((kbytes + BKB - 1) / BKB);
+    const int c = tid % CPR, r0 = tid / CPR;
+    const int lds0 = r0 * BKB + ((c ^ swz<CPR>(r0)) * 16);
+
+    i32x4 RA[A_PER_T], RB[8];
+    auto load = [&](int kt) {
+        const int64_t ka = (int64_t)kt * BKB + c * 16;
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i) {
+            const int gr = row0 + r0 + i * RS;
+            const bool ok = gr < p.M;
+            RA[i] = load_chunk_masked(p.A + (int64_t)(ok ? gr : 0) * p.lda_b, ka, kbytes, ok);
+        }
+        const int64_t k0 = (int64_t)kt * KPS;   // the stage's first B^T row
+        const int64_t colb = P == PREC_F16 ? 2 * (int64_t)col0 : (P == PREC_I8 ? col0 : col0 / 2);
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const int q = tid + i * NT;
+            const int kl = (q / CPB) * ROWS, nc = q % CPB;
+            const int64_t off = colb + nc * 16;
+#pragma unroll
+            for (int h = 0; h < ROWS; ++h) {
+                const int64_t k = k0 + kl + h;
+                const bool ok = k < K;
+                RB[i * ROWS + h] = load_chunk_masked(p.B + (ok ? k : 0) * p.ldb_b, off, nbytes, ok);
+            }
+        }
+    };
+    auto store = [&](int stage) {
+        uint8_t *S = smem + stage * STAGE;
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i)
+            *reinterpret_cast<i32x4 *>(S + lds0 + i * RS * BKB) = RA[i];
+        uint8_t *SB = S + BM * BKB;
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const int q = tid + i * NT;
+            const int kl = (q / CPB) * ROWS, nc = q % CPB;
+            // byte of the [n][k] row that this item's k lands in
+            const int kb = P == PREC_F16 ? 2 * kl : (P == PREC_I8 ? kl : kl / 2);
+            const int kc = kb >> 4, kw = kb & 15;
+#pragma unroll
+            for (int e = 0; e < NPC; ++e) {
+                const int r = nc * NPC + e;
+                uint8_t *dst = SB + r * BKB + ((kc ^ swz<CPR>(r)) << 4) + kw;
+                if constexpr (P == PREC_F16) {
+                    const uint32_t w = (uint32_t)RB[i][e >> 1];
+                    *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(w >> (16 * (e & 1)));
+                } else if constexpr (P == PREC_I8) {
+                    *dst = (uint8_t)((uint32_t)RB[i][e >> 2] >> (8 * (e & 3)));
+                } else {
+                    // nibble e of the chunks of rows k (low) and k + 1 (high)
+                    const uint32_t lo = (uint32_t)RB[2 * i][e >> 3] >> (4 * (e & 7));
+                    const uint32_t hi = (uint32_t)RB[2 * i + 1][e >> 3] >> (4 * (e & 7));
+                    *dst = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+                }
+            }
+        }
+    };
+
+    acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = acc_t{};
+    if (KT > 0) {
+        load(0);
+        store(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT)
+            load(kt + 1);
+#pragma unroll
+        for (int step = 0; step < CPR / 2; ++step) {
+            i32x4 fa[TM], fb[TN];
+            read_frags<BM, BKB, TM, TN>(smem + cur * STAGE, step, wm0, wn0, lane, fa, fb);
+            mfma_step<P, TM, TN>(fa, fb, acc);
+        }
+        if (kt + 1 < KT)
+            store(cur ^ 1);
+        __syncthreads();
+    }
+    store_tile<P, TM, TN>(p, row0 + wm0, col0 + wn0, lane, acc);
+}
+
 // ------------------------------------------------------------------ launch
 
 // BM x BN tile, BKB bytes of K per stage, blocks that one compute unit holds
@@ -1241,6 +1366,18 @@ static hipError_t launch_prec(int cfg, const GemmProblem &p, const StreamKPlan &
     case CFG_256x256_DTV: return launch_dtv<P, 2>(p, sk, ws, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemm_kn(int prec, const GemmProblem &p, hipStream_t stream) {
+    const int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
+    const dim3 grid(tiles_m * tiles_n), block(256);
+    switch (prec) {
+    case PREC_F16: hipLaunchKernelGGL(gemm_tile_kn_kernel<PREC_F16>, grid, block, 0, stream, p, tiles_m, tiles_n); break;
+    case PREC_I8: hipLaunchKernelGGL(gemm_tile_kn_kernel<PREC_I8>, grid, block, 0, stream, p, tiles_m, tiles_n); break;
+    case PREC_I4: hipLaunchKernelGGL(gemm_tile_kn_kernel<PREC_I4>, grid, block, 0, stream, p, tiles_m, tiles_n); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm(int prec, int cfg, const GemmProblem &p, const StreamKPlan &sk,

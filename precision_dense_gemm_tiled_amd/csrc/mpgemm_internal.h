@@ -89,6 +89,9 @@ struct StreamKPlan {
 enum StreamKMode { SK_MODE_AUTO = -1, SK_MODE_OFF = 0, SK_MODE_ON = 1 };
 StreamKPlan plan_stream_k(int cfg, int64_t M, int64_t N, int64_t kbytes, int cu_count,
                           int64_t partial_bytes, int flag_count, int mode);
+// Transposed-B control: B (the B^T of the K x N layout) rows are k, ldb_b
+// their byte stride; 16-byte aligned operands; PREC_F16, PREC_I8, PREC_I4.
+hipError_t launch_gemm_kn(int prec, const GemmProblem &p, hipStream_t stream);
 hipError_t launch_gemm(int prec, int cfg, const GemmProblem &p, const StreamKPlan &sk,
                        const TileWorkspace &ws, hipStream_t stream);
 

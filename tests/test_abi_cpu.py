@@ -30,7 +30,8 @@ def declared_symbols():
 def test_header_declares_the_abi():
     names = declared_symbols()
     for n in ["mpgemm_create", "mpgemm_destroy", "mpgemm_status_string", "mpgemm_run_f16",
-              "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_run_w4a4", "mpgemm_quantize_w4"]:
+              "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_run_w4a4", "mpgemm_quantize_w4",
+              "mpgemm_run_f16_kn", "mpgemm_run_i8_kn", "mpgemm_run_i4_kn"]:
         assert n in names
 
 
@@ -97,6 +98,34 @@ A, B, C, S = 0x10000, 0x20000, 0x30000, 0x40000
 def test_gemm_argument_errors_without_device(mp, call, expect):
     prec, *args = call
     f = {"i8": mp.mpgemm_run_i8, "i4": mp.mpgemm_run_i4, "f16": mp.mpgemm_run_f16}[prec]
+    assert f(None, *args, None) == expect
+
+
+@pytest.mark.parametrize("call,expect", [
+    # sizes, no-ops, pointers
+    (("i8", -1, 16, 16, A, 16, B, 16, C, 16), 1),
+    (("i8", 0, 16, 16, 0, 16, 0, 16, 0, 16), 0),
+    (("f16", 4, 16, 16, A, 16, 0, 16, C, 16), 1),
+    # Bt is K x N: its leading dimension is checked against N, not K
+    (("i8", 4, 32, 16, A, 16, B, 16, C, 32), 1),
+    (("i8", 4, 16, 32, A, 32, B, 16, C, 16), 1),      # ldbt = N < K is fine: NULL handle left
+    (("f16", 4, 16, 16, A, 8, B, 16, C, 16), 1),      # lda < K
+    # one kernel only: 16-byte rows and bases, else unsupported
+    (("i8", 4, 16, 16, A, 16, B + 8, 16, C, 16), 2),
+    (("i8", 4, 16, 16, A, 24, B, 16, C, 16), 2),
+    (("f16", 4, 12, 16, A, 16, B, 12, C, 12), 2),     # Bt rows of 24 bytes
+    (("f16", 4, 16, 16, A, 16, B, 16, C + 2, 16), 2),
+    # INT4: K, lda, ldbt even; Bt rows of ldbt / 2 bytes, a multiple of 16
+    (("i4", 4, 32, 31, A, 32, B, 32, C, 32), 2),
+    (("i4", 4, 31, 32, A, 32, B, 33, C, 32), 2),
+    (("i4", 4, 31, 32, A, 32, B, 48, C, 32), 2),
+    (("i4", 4, 31, 32, A, 32, B, 32, C, 32), 1),      # odd N: NULL handle left
+    # integer K bound
+    (("i8", 4, 16, 131072, A, 131072, B, 16, C, 16), 2),
+])
+def test_gemm_kn_argument_errors_without_device(mp, call, expect):
+    prec, *args = call
+    f = {"i8": mp.mpgemm_run_i8_kn, "i4": mp.mpgemm_run_i4_kn, "f16": mp.mpgemm_run_f16_kn}[prec]
     assert f(None, *args, None) == expect
 
 

@@ -114,6 +114,46 @@ def test_whole_stage_config(prec, cfg, M, N, kb, monkeypatch):
     assert np.array_equal(runs[0].view(np.uint32), runs[1].view(np.uint32)), "repeat differs"
 
 
+# Transposed-B layout (B stored K x N), the control of the B-layout ablation:
+# ragged M and N tiles with a K tail inside a stage, exactly one stage,
+# several stages, a single output row, odd N (INT4 packs two n per byte),
+# K = 0 (C = 0).
+KN_SHAPES = [(300, 520, 200), (256, 256, 256), (513, 260, 1024), (1, 40, 64), (33, 47, 64), (70, 90, 0)]
+
+
+def _padded_rows(a):
+    """2-D host array -> device view of the same values whose rows start on
+    16-byte boundaries (row stride padded with zeros)."""
+    rows, width = a.shape
+    pad = -(-max(width * a.itemsize, 1) // 16) * 16 // a.itemsize
+    buf = np.zeros((max(rows, 2), pad), dtype=a.dtype)
+    buf[:rows, :width] = a
+    return dev(buf)[:rows, :width]
+
+
+@pytest.mark.parametrize("prec", ["i8", "i4", "f16"])
+@pytest.mark.parametrize("M,N,K", KN_SHAPES)
+def test_transposed_b_layout(prec, M, N, K):
+    """mpgemm_run_*_kn against the oracle of the usual N x K layout on the
+    same values: Bt is B transposed (INT4: repacked two n per byte)."""
+    if prec == "i4" and K % 2:
+        pytest.skip("INT4 K is even")
+    A, B = inputs.gemm_problem(prec, M, N, K, seed=5000 + M + N + K)
+    ref = _ref(prec, A, B, K)
+    if prec == "i4":
+        vals = unpack_i4(B, K).T                     # K x N values
+        if N % 2:
+            vals = np.concatenate([vals, np.zeros((K, 1), dtype=vals.dtype)], axis=1)
+        bt = pack_i4(vals) if K else np.zeros((0, (N + 1) // 2), dtype=np.uint8)
+        got = host(mp.gemm_i4_kn(_padded_rows(A), _padded_rows(bt), N))
+    else:
+        bt = np.ascontiguousarray(B.T)
+        f = mp.gemm_i8_kn if prec == "i8" else mp.gemm_f16_kn
+        got = host(f(_padded_rows(A), _padded_rows(bt)))
+    assert got.shape == (M, N)
+    _compare(prec, got, ref, max(K, 1), f"{prec} kn {M}x{N}x{K}")
+
+
 def test_i4_equals_i8_of_unpacked_on_gpu():
     M, N, K = 190, 260, 384
     Ap, Bp = inputs.gemm_problem("i4", M, N, K, seed=4242)
