@@ -241,8 +241,10 @@ __device__ __forceinline__ void stage_factors(const GemmProblem &p, int row0, in
 // A row of the stage, the second half every B row); 2 the tile loads marked
 // non-temporal (nt); 3 the tile loads at device scope (sc1); 4 tile loads
 // staged through VGPRs (global_load_dwordx4, then ds_write_b128 into the free
-// stage before the barrier that publishes it) instead of direct-to-LDS.
-enum { VAR_BASE = 0, VAR_SPLIT = 1, VAR_NT = 2, VAR_SC1 = 3, VAR_VGPR = 4, VAR_SPREAD = 5 };
+// stage before the barrier that publishes it) instead of direct-to-LDS;
+// 5 the next entry's loads spread over the k-steps; 6 the tile loads with
+// the sc0 cache-policy bit.
+enum { VAR_BASE = 0, VAR_SPLIT = 1, VAR_NT = 2, VAR_SC1 = 3, VAR_VGPR = 4, VAR_SPREAD = 5, VAR_SC0 = 6 };
 
 template <int AUX>
 __device__ __forceinline__ void dma16_cp(const void *g, void *lds) {
@@ -264,7 +266,7 @@ struct RingTile {
     // SPREAD: the next entry's loads are issued a few per k-step, between the
     // fragment reads and MFMAs, instead of all at the top of the iteration
     static constexpr bool SPREAD = VAR == VAR_SPREAD;
-    static constexpr int CPOL = VAR == VAR_NT ? 2 : (VAR == VAR_SC1 ? 16 : 0);
+    static constexpr int CPOL = VAR == VAR_NT ? 2 : (VAR == VAR_SC1 ? 16 : (VAR == VAR_SC0 ? 1 : 0));
     static constexpr int RSL = SPLIT ? RS / 2 : RS;   // rows per load round of one loader
     static constexpr int HW = NT / 128;                // wavefronts per operand when split
     static_assert(!SPLIT || (BM == BN && (NT / 2) % 64 == 0 && RSL % 16 == 0), "split loaders");
@@ -1205,6 +1207,7 @@ static const CfgShape kCfg[CFG_COUNT] = {
     {256, 256, 128, 1, "256x256_bk128_ring2_vgpr_staged"},
     {256, 256, 128, 1, "256x256_bk128_ring2_spread_loads"},
     {256, 256, 128, 1, "256x256_bk128_a_ring2_b_direct"},
+    {256, 256, 128, 1, "256x256_bk128_ring2_sc0"},
 };
 
 const char *tile_cfg_name(int cfg) {
@@ -1364,6 +1367,7 @@ static hipError_t launch_prec(int cfg, const GemmProblem &p, const StreamKPlan &
     case CFG_256x256_VGPR: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_VGPR>(p, sk, ws, stream);
     case CFG_256x256_SPREAD: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_SPREAD>(p, sk, ws, stream);
     case CFG_256x256_DTV: return launch_dtv<P, 2>(p, sk, ws, stream);
+    case CFG_256x256_SC0: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_SC0>(p, sk, ws, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -48,6 +48,7 @@ enum TileCfg {
     CFG_256x256_VGPR = 16,  // tile loads staged through VGPRs instead of direct-to-LDS
     CFG_256x256_SPREAD = 17,// the next stage's loads issued a few per k-step instead of all at once
     CFG_256x256_DTV = 18,   // B straight from global memory into MFMA registers, only A through LDS
+    CFG_256x256_SC0 = 19,   // (ablation of CFG_256x256_BK128) tile loads with the sc0 cache-policy bit
     CFG_COUNT
 };
 

@@ -7,8 +7,8 @@ import numpy as np
 # override): 0-11 the ring kernel's shapes, 12 the 256 x 256 ping-pong kernel,
 # 13-17 one-change ablations of the 256 x 256 ring (split loaders, nt, sc1,
 # VGPR-staged loads, spread loads), 18 the 256 x 256 kernel with B loaded
-# straight into registers.
-N_TILE_CFGS = 19
+# straight into registers, 19 the sc0 cache-policy ablation of the ring.
+N_TILE_CFGS = 20
 PINGPONG_CFG = 12
 B_DIRECT_CFGS = (18,)
 
