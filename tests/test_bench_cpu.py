@@ -1,5 +1,6 @@
 """Host-side logic of bench.py (no GPU): the one-GPU refusal, the roofline
-arithmetic, the algorithmic byte counts and the traffic profile's guard."""
+arithmetic, the algorithmic byte counts, the traffic profile's guard and the
+K x N operand of the transposed-B control."""
 import os
 import subprocess
 import sys
@@ -63,3 +64,31 @@ def test_traffic_profile_guard(tmp_path, monkeypatch):
     # and so is a missing one
     monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(tmp_path / "absent.md"))
     assert bench.measured_traffic() is None
+
+
+@pytest.mark.parametrize("prec,N,K", [("i8", 40, 64), ("f16", 24, 16), ("i4", 47, 64), ("i4", 64, 32)])
+def test_transposed_b_operand_by_element(prec, N, K):
+    """bench.transpose_b (the K x N operand of the transposed-B control) holds
+    B[n][k] at row k, column n; for INT4 element n of row k is nibble n % 2
+    of byte n / 2 (low nibble = even n), two's complement."""
+    import numpy as np
+    from precision_dense_gemm_tiled_amd import inputs
+    _, B = inputs.gemm_problem(prec, 3, N, K, seed=N + K)
+    bt = bench.transpose_b(prec, B, N, K)
+    if prec != "i4":
+        assert bt.shape == (K, N) and bt.flags["C_CONTIGUOUS"]
+        for n in range(N):
+            for k in range(K):
+                assert bt[k, n] == B[n, k] or (np.isnan(bt[k, n]) and np.isnan(B[n, k]))
+        return
+
+    def nib(byte, hi):
+        v = (int(byte) >> (4 * hi)) & 0xF
+        return v - 16 if v >= 8 else v
+
+    assert bt.shape == (K, (N + 1) // 2)
+    for n in range(N):
+        for k in range(K):
+            assert nib(bt[k, n // 2], n % 2) == nib(B[n, k // 2], k % 2), (n, k)
+    if N % 2:
+        assert not np.any(bt[:, -1] >> 4)   # the padding nibble is zero
