@@ -255,13 +255,14 @@ def time_graph(prob, launches, replays):
     return start.elapsed_time(stop) / 1e3 / (replays * launches)
 
 
-def sweep_entry(prec, M, N, K, seed, steps, warmup, eager=False, b_layout="nk"):
+def sweep_entry(prec, M, N, K, seed, steps, warmup, eager=False, b_layout="nk", launches=None):
     copies = copies_for_cold(prec, M, N, K)
     p = Problem(prec, M, N, K, seed, copies, b_layout)
-    # expected kernel time at ~30% of the roofline sets the launches per graph
-    est_s = max(roofline(prec, M, N, K, 1.0)["ops"] / (PEAK.get(prec, 2500.0) * 1e12 * 0.3),
-                algorithmic_bytes(prec, M, N, K) / (HBM_GBS * 1e9 * 0.3))
-    launches = int(min(max(len(p.ins), 0.02 / max(est_s, 1e-7)), 2048))
+    if launches is None:
+        # expected kernel time at ~30% of the roofline sets the launches per graph
+        est_s = max(roofline(prec, M, N, K, 1.0)["ops"] / (PEAK.get(prec, 2500.0) * 1e12 * 0.3),
+                    algorithmic_bytes(prec, M, N, K) / (HBM_GBS * 1e9 * 0.3))
+        launches = int(min(max(len(p.ins), 0.02 / max(est_s, 1e-7)), 2048))
     launches = max(launches, 2)
     if eager:
         # one launch at a time (for counter collection, which does not follow
@@ -357,6 +358,9 @@ def main():
                          "transposed-B control, mpgemm_run_*_kn)")
     ap.add_argument("--eager", action="store_true",
                     help="time the sweep with eager launches instead of HIP graph replay")
+    ap.add_argument("--launches", type=int, default=None,
+                    help="with --only: launches per timed batch (default: enough for ~20 ms); "
+                         "counter collection uses a few eager launches")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 256 MiB device copy (reference dispatch for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -396,7 +400,8 @@ def main():
                 M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else ((1, s, s) if prec == "quantize" else (s, s, s))
                 seed = inputs.config_seed(CONFIG_INDEX[prec], s)
                 layout = args.b_layout if prec in ("f16", "i8", "i4") else "nk"
-                e = sweep_entry(prec, M, N, K, seed, args.steps, args.warmup, args.eager, layout)
+                e = sweep_entry(prec, M, N, K, seed, args.steps, args.warmup, args.eager, layout,
+                                args.launches)
                 log(prec, e)
                 out[prec].append(e)
         print(json.dumps(out))

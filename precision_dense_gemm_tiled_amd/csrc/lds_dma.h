@@ -25,6 +25,13 @@ __device__ __forceinline__ void wait_vm_lds() {
     __builtin_amdgcn_s_waitcnt(imm);
 }
 
+// s_waitcnt for "all LDS operations done", vector-memory loads left in
+// flight (vmcnt at its maximum).
+__device__ __forceinline__ void wait_lds_only() {
+    constexpr int imm = 15 | (3 << 14) | (7 << 4);
+    __builtin_amdgcn_s_waitcnt(imm);
+}
+
 // Workgroup barrier that publishes LDS-DMA data without waiting for every
 // outstanding load: the caller's wait_vm_lds<> decides which loads must have
 // landed. Compiler-level fences keep memory operations on their side.

@@ -49,6 +49,7 @@ enum TileCfg {
     CFG_256x256_SPREAD = 17,// the next stage's loads issued a few per k-step instead of all at once
     CFG_256x256_DTV = 18,   // B straight from global memory into MFMA registers, only A through LDS
     CFG_256x256_SC0 = 19,   // (ablation of CFG_256x256_BK128) tile loads with the sc0 cache-policy bit
+    CFG_256x256_EARLY = 20, // (ablation of CFG_256x256_BK128) fragment reads fenced ahead of each k-step's MFMAs
     CFG_COUNT
 };
 

@@ -7,8 +7,9 @@ import numpy as np
 # override): 0-11 the ring kernel's shapes, 12 the 256 x 256 ping-pong kernel,
 # 13-17 one-change ablations of the 256 x 256 ring (split loaders, nt, sc1,
 # VGPR-staged loads, spread loads), 18 the 256 x 256 kernel with B loaded
-# straight into registers, 19 the sc0 cache-policy ablation of the ring.
-N_TILE_CFGS = 20
+# straight into registers, 19 the sc0 cache-policy ablation of the ring, 20
+# the ring with each k-step's fragment reads fenced ahead of its MFMAs.
+N_TILE_CFGS = 21
 PINGPONG_CFG = 12
 B_DIRECT_CFGS = (18,)
 
@@ -78,8 +79,13 @@ def freivalds_int(C: np.ndarray, A: np.ndarray, B: np.ndarray, seed: int, trials
         assert bad.size == 0, f"Freivalds mismatch in rows {bad[:8]}"
 
 
-def sample_rows(M: int, count: int, seed: int) -> np.ndarray:
-    """First, last and random rows."""
-    rng = np.random.default_rng(seed)
-    rows = set([0, M - 1]) | set(rng.integers(0, M, size=max(count - 2, 0)).tolist())
-    return np.array(sorted(rows))
+def band_rows(M: int, band: int, per_band: int) -> np.ndarray:
+    """per_band rows in each band of `band` consecutive rows, at offsets
+    within the band that differ from band to band (a fixed odd stride), so
+    together they reach many row positions of an output tile."""
+    rows = []
+    for b0 in range(0, M, band):
+        size = min(band, M - b0)
+        for j in range(per_band):
+            rows.append(b0 + ((b0 // band) * 37 + j * (size // per_band + 1)) % size)
+    return np.array(sorted(set(rows)))
