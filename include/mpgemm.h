@@ -187,6 +187,30 @@ mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_
                                  const uint16_t *S, int64_t lds, int64_t group_size,
                                  uint16_t *Y, int64_t ldy, void *stream);
 
+/* Allocation-free weight-only INT4 GEMM, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. No handle: it runs on the caller's
+ * current device, computes exactly what mpgemm_run_w4a16 computes with a
+ * default handle (the same kernel plan, so bit-identical results), and takes
+ * the same arguments with the same meaning, layout and checks.
+ * The fp32 partial sums of a K split live in a static device array of
+ * MPGEMM_NOALLOC_SCRATCH_BYTES per GPU (held by each GPU the library runs on
+ * until the process ends); no call allocates or frees memory. A problem whose
+ * split needs more than that returns MPGEMM_ERR_UNSUPPORTED before any
+ * launch. Every call on one GPU shares that GPU's array, and each call
+ * overwrites every partial sum it reads, so consecutive calls need no reset;
+ * calls that overlap in time on one GPU (concurrent streams, or host
+ * threads) race on the array and give undefined results: order them on one
+ * stream. The first call on a device looks up that device's copy of the
+ * array (MPGEMM_ERR_HIP if that fails); MPGEMM_ERR_DEVICE without a current
+ * device. */
+#define MPGEMM_NOALLOC_SCRATCH_BYTES (16 << 20)
+mpgemm_status_t mpgemm_run_w4a16_noalloc(int64_t M, int64_t N, int64_t K,
+                                         const uint16_t *X, int64_t ldx,
+                                         const uint8_t *Wq, int64_t ldw,
+                                         const uint16_t *S, int64_t lds, int64_t group_size,
+                                         uint16_t *Y, int64_t ldy, void *stream);
+
 /* Weight quantisation for mpgemm_run_w4a16 (the weights and scales it
  * consumes: "fused-int4-gemm-sm75" README, feature list: per-group scaling
  * factors, group_size = 128, packed INT4 weights; the README names no

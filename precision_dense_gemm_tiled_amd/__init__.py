@@ -14,9 +14,11 @@ __all__ = [
     "MpgemmError", "lib", "lib_path",
     "mpgemm_create", "mpgemm_destroy", "mpgemm_status_string",
     "mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_run_w4a4", "mpgemm_quantize_w4",
+    "mpgemm_run_w4a16_noalloc",
     "mpgemm_run_f16_kn", "mpgemm_run_i8_kn", "mpgemm_run_i4_kn",
     "mpgemm_plan_gemm", "mpgemm_plan_w4a16",
     "Handle", "default_handle", "gemm_f16", "gemm_i8", "gemm_i4", "gemm_w4a16", "gemm_w4a4", "quantize_w4",
+    "gemm_w4a16_noalloc",
     "gemm_f16_kn", "gemm_i8_kn", "gemm_i4_kn",
 ]
 
@@ -65,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.mpgemm_run_w4a16.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
                                        _vp, _i64, _i64, _vp, _i64, _vp]
         L.mpgemm_run_w4a16.restype = ctypes.c_int
+        L.mpgemm_run_w4a16_noalloc.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64,
+                                               _vp, _i64, _i64, _vp, _i64, _vp]
+        L.mpgemm_run_w4a16_noalloc.restype = ctypes.c_int
         L.mpgemm_run_w4a4.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
                                       _vp, _i64, _vp]
         L.mpgemm_run_w4a4.restype = ctypes.c_int
@@ -124,6 +129,10 @@ def mpgemm_run_i4_kn(h, M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None) -> int:
 
 def mpgemm_run_w4a16(h, M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, stream=None) -> int:
     return lib().mpgemm_run_w4a16(h, M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, stream)
+
+
+def mpgemm_run_w4a16_noalloc(M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, stream=None) -> int:
+    return lib().mpgemm_run_w4a16_noalloc(M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, stream)
 
 
 def mpgemm_run_w4a4(h, M, N, K, A, lda, B, ldb, SX, SW, bias, Y, ldy, stream=None) -> int:
@@ -324,6 +333,24 @@ def gemm_w4a16(X, Wq, S, group_size, out=None, handle=None, stream=None):
     _check(mpgemm_run_w4a16(h, M, N, K, X.data_ptr(), ldx, Wq.data_ptr(), 2 * ldw_b,
                             S.data_ptr(), lds, group_size, Y.data_ptr(), ldy, _stream(stream)),
            "mpgemm_run_w4a16")
+    return Y
+
+
+def gemm_w4a16_noalloc(X, Wq, S, group_size, out=None, stream=None):
+    """gemm_w4a16 through the allocation-free entry point (no handle; the
+    current device's static scratch; `out` preallocated by the caller when
+    nothing may be allocated)."""
+    import torch
+    ldx = _rows(X, torch.float16, "X")
+    ldw_b = _rows(Wq, torch.uint8, "Wq")
+    lds = _rows(S, torch.float16, "S")
+    M, K = X.shape
+    N = Wq.shape[0]
+    Y = torch.empty((M, N), dtype=torch.float16, device=X.device) if out is None else out
+    ldy = _rows(Y, torch.float16, "Y")
+    _check(mpgemm_run_w4a16_noalloc(M, N, K, X.data_ptr(), ldx, Wq.data_ptr(), 2 * ldw_b,
+                                    S.data_ptr(), lds, group_size, Y.data_ptr(), ldy, _stream(stream)),
+           "mpgemm_run_w4a16_noalloc")
     return Y
 
 

@@ -183,6 +183,66 @@ mpgemm_status_t run_kn(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int64_
 
 }  // namespace
 
+namespace mpg {
+
+// Every argument check of a weight-only call except the handle (shared with
+// the allocation-free entry point).
+mpgemm_status_t check_w4a16_args(int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t ldx,
+                                 const uint8_t *Wq, int64_t ldw, const uint16_t *S, int64_t lds,
+                                 int64_t group_size, const uint16_t *Y, int64_t ldy, bool *noop) {
+    *noop = false;
+    if (M < 0 || N < 0 || K < 0)
+        return MPGEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return MPGEMM_OK;
+    }
+    if (!Y || (K > 0 && (!X || !Wq || !S)))
+        return MPGEMM_ERR_INVALID_ARG;
+    if (ldx < K || ldw < K || ldy < N)
+        return MPGEMM_ERR_INVALID_ARG;
+    const bool pow2 = group_size > 0 && (group_size & (group_size - 1)) == 0;
+    if (K > 0) {
+        if (!pow2 || group_size < 32 || group_size > K || K % group_size != 0)
+            return MPGEMM_ERR_UNSUPPORTED;
+        if (lds < K / group_size)
+            return MPGEMM_ERR_INVALID_ARG;
+    }
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX || (M + 31) / 32 > 65535)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if ((ldw % 2) != 0)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if ((K > 0 && (!aligned16(X) || !aligned16(Wq) || (reinterpret_cast<uintptr_t>(S) & 1u))) ||
+        (reinterpret_cast<uintptr_t>(Y) & 1u))
+        return MPGEMM_ERR_UNSUPPORTED;
+    if ((ldx * 2) % 16 != 0 || (ldw / 2) % 16 != 0)
+        return MPGEMM_ERR_UNSUPPORTED;
+    return MPGEMM_OK;
+}
+
+W4A16Problem make_w4a16_problem(int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t ldx,
+                                const uint8_t *Wq, int64_t ldw, const uint16_t *S, int64_t lds,
+                                int64_t group_size, uint16_t *Y, int64_t ldy) {
+    W4A16Problem p;
+    p.X = X;
+    p.W = Wq;
+    p.S = S;
+    p.Y = Y;
+    p.ldx = ldx;
+    p.ldw_b = ldw / 2;
+    p.lds = lds;
+    p.ldy = ldy;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.G = K > 0 ? (int)group_size : 32;
+    return p;
+}
+
+int64_t w4a16_split_floats() { return kSplitPartialFloats; }
+
+}  // namespace mpg
+
 extern "C" {
 
 mpgemm_status_t mpgemm_create(mpgemm_handle_t *out, int device) {
@@ -375,48 +435,16 @@ mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_
                                  const uint16_t *X, int64_t ldx, const uint8_t *Wq, int64_t ldw,
                                  const uint16_t *S, int64_t lds, int64_t group_size,
                                  uint16_t *Y, int64_t ldy, void *stream) {
-    if (M < 0 || N < 0 || K < 0)
-        return MPGEMM_ERR_INVALID_ARG;
-    if (M == 0 || N == 0)
-        return MPGEMM_OK;
-    if (!Y || (K > 0 && (!X || !Wq || !S)))
-        return MPGEMM_ERR_INVALID_ARG;
-    if (ldx < K || ldw < K || ldy < N)
-        return MPGEMM_ERR_INVALID_ARG;
-    const bool pow2 = group_size > 0 && (group_size & (group_size - 1)) == 0;
-    if (K > 0) {
-        if (!pow2 || group_size < 32 || group_size > K || K % group_size != 0)
-            return MPGEMM_ERR_UNSUPPORTED;
-        if (lds < K / group_size)
-            return MPGEMM_ERR_INVALID_ARG;
-    }
-    if (M > INT_MAX || N > INT_MAX || K > INT_MAX || (M + 31) / 32 > 65535)
-        return MPGEMM_ERR_UNSUPPORTED;
-    if ((ldw % 2) != 0)
-        return MPGEMM_ERR_UNSUPPORTED;
-    if ((K > 0 && (!aligned16(X) || !aligned16(Wq) || (reinterpret_cast<uintptr_t>(S) & 1u))) ||
-        (reinterpret_cast<uintptr_t>(Y) & 1u))
-        return MPGEMM_ERR_UNSUPPORTED;
-    if ((ldx * 2) % 16 != 0 || (ldw / 2) % 16 != 0)
-        return MPGEMM_ERR_UNSUPPORTED;
+    bool noop;
+    mpgemm_status_t st = mpg::check_w4a16_args(M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy, &noop);
+    if (st != MPGEMM_OK || noop)
+        return st;
     if (!h)
         return MPGEMM_ERR_INVALID_ARG;
     DeviceGuard dg(h->device);
     if (!dg.ok)
         return MPGEMM_ERR_HIP;
-    mpg::W4A16Problem p;
-    p.X = X;
-    p.W = Wq;
-    p.S = S;
-    p.Y = Y;
-    p.ldx = ldx;
-    p.ldw_b = ldw / 2;
-    p.lds = lds;
-    p.ldy = ldy;
-    p.M = (int)M;
-    p.N = (int)N;
-    p.K = (int)K;
-    p.G = K > 0 ? (int)group_size : 32;
+    const mpg::W4A16Problem p = mpg::make_w4a16_problem(M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ldy);
     const int cfg = h->forced_w4a16_cfg >= 0 ? h->forced_w4a16_cfg : mpg::choose_w4a16_cfg(M, N, K);
     const mpg::W4A16Plan plan = mpg::plan_w4a16(M, N, K, cfg, h->cu_count, h->ws.partial_floats);
     hipError_t e = mpg::launch_w4a16(p, plan, h->ws, static_cast<hipStream_t>(stream));

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mpgemm.h"
+
 namespace mpg {
 
 // PREC_W4A4: the INT4 main loop with a scale epilogue (fp16 output).
@@ -152,6 +154,20 @@ struct W4A16Plan {
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cfg, int cu_count, int64_t partial_floats);
 hipError_t launch_w4a16(const W4A16Problem &p, const W4A16Plan &plan, const W4A16Workspace &ws,
                         hipStream_t stream);
+
+// Argument checks of a weight-only call (all but the handle; *noop set for
+// M == 0 or N == 0) and the problem they describe; shared by the handle and
+// the allocation-free entry points. w4a16_split_floats: the fp32 slice
+// capacity a handle gives the K split (the plan both entry points use).
+mpgemm_status_t check_w4a16_args(int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t ldx,
+                                 const uint8_t *Wq, int64_t ldw, const uint16_t *S, int64_t lds,
+                                 int64_t group_size, const uint16_t *Y, int64_t ldy, bool *noop);
+W4A16Problem make_w4a16_problem(int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t ldx,
+                                const uint8_t *Wq, int64_t ldw, const uint16_t *S, int64_t lds,
+                                int64_t group_size, uint16_t *Y, int64_t ldy);
+int64_t w4a16_split_floats();
+// Bytes of fp32 K slices a plan writes (0: no split).
+int64_t w4a16_plan_scratch_floats(const W4A16Plan &plan);
 
 // Symmetric INT4 quantisation of fp16 weights per (row, G-wide K group).
 struct QuantizeW4Problem {

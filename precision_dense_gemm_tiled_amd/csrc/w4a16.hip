@@ -1190,6 +1190,21 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cfg, int cu_count, int
     return plan;
 }
 
+int64_t w4a16_plan_scratch_floats(const W4A16Plan &plan) {
+    if (plan.ks <= 1)
+        return 0;
+    switch (plan.cfg) {
+#define MPG_SCRATCH(C, mb, nb, wn, wk, nst) \
+    case C: return (int64_t)plan.ks * plan.mblocks * plan.ngroups * (16 * mb) * (16 * nb * wn);
+        MPG_SLICE_CONFIGS(MPG_SCRATCH)
+#undef MPG_SCRATCH
+    case W4A16_RING3_128x64:
+    case W4A16_RING4_128x64:
+        return (int64_t)plan.ks * plan.mblocks * RG_BM * plan.ngroups * RG_BN;
+    default: return 0;
+    }
+}
+
 const char *w4a16_cfg_name(int cfg) {
     static const char *names[W4A16_CFG_COUNT] = {
         "mfma 16 rows x 16 cols, K split 4", "mfma 32 x 64 tile",

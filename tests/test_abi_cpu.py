@@ -148,6 +148,30 @@ def test_w4a16_argument_errors_without_device(mp, args, expect):
 
 
 @pytest.mark.parametrize("args,expect", [
+    ((1, 16, 256, A, 256, B, 256, S, 2, 100, C, 16), 2),     # G not a power of two
+    ((1, 16, 192, A, 256, B, 256, S, 2, 128, C, 16), 2),     # K % G != 0
+    ((1, 16, 256, A, 256, B, 256, S, 1, 128, C, 16), 1),     # lds < K/G
+    ((1, 16, 256, A, 256, B, 250, S, 2, 128, C, 16), 1),     # ldw < K
+    ((1, 16, 256, A + 2, 256, B, 256, S, 2, 128, C, 16), 2),  # X not 16-byte aligned
+    ((1, 16, 256, A, 256, B, 256, S, 2, 128, C + 1, 16), 2),  # Y not 2-byte aligned
+    ((-1, 16, 256, A, 256, B, 256, S, 2, 128, C, 16), 1),    # negative size
+    ((1, 16, 256, 0, 256, B, 256, S, 2, 128, C, 16), 1),     # NULL activations
+    ((0, 16, 256, 0, 256, 0, 256, 0, 2, 128, 0, 16), 0),     # M = 0: no-op
+])
+def test_w4a16_noalloc_argument_errors_without_device(mp, args, expect):
+    """The allocation-free entry point makes the same argument checks as
+    mpgemm_run_w4a16, before any HIP call."""
+    assert mp.mpgemm_run_w4a16_noalloc(*args, None) == expect
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present")
+def test_w4a16_noalloc_without_gpu_reports_device_error(mp):
+    """With valid arguments and no GPU, the device query fails first."""
+    args = (1, 16, 256, A, 256, B, 256, S, 2, 128, C, 16)
+    assert mp.mpgemm_run_w4a16_noalloc(*args, None) == mp.MPGEMM_ERR_DEVICE
+
+
+@pytest.mark.parametrize("args,expect", [
     ((16, 256, A, 256, 128, B, 256, S, 2), 1),       # valid: NULL handle left
     ((-1, 256, A, 256, 128, B, 256, S, 2), 1),      # negative size
     ((0, 256, 0, 256, 128, 0, 256, 0, 2), 0),       # N = 0: no-op
