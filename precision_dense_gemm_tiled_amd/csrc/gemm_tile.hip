@@ -246,9 +246,11 @@ __device__ __forceinline__ void stage_factors(const GemmProblem &p, int row0, in
 // stage before the barrier that publishes it) instead of direct-to-LDS;
 // 5 the next entry's loads spread over the k-steps; 6 the tile loads with
 // the sc0 cache-policy bit; 7 each k-step's fragment reads fenced ahead of
-// the previous step's MFMAs.
+// the previous step's MFMAs; 8 each k-step's fragment reads woven two per
+// MFMA between its first MFMAs (and step 0's direct-to-LDS loads two per MFMA
+// after them).
 enum { VAR_BASE = 0, VAR_SPLIT = 1, VAR_NT = 2, VAR_SC1 = 3, VAR_VGPR = 4, VAR_SPREAD = 5, VAR_SC0 = 6,
-       VAR_EARLY = 7 };
+       VAR_EARLY = 7, VAR_WEAVE = 8 };
 
 template <int AUX>
 __device__ __forceinline__ void dma16_cp(const void *g, void *lds) {
@@ -278,6 +280,7 @@ struct RingTile {
     // 8192 (INT8, FP16, INT4): the matrix unit idles while a wavefront
     // issues its reads ahead of its MFMAs.
     static constexpr bool EARLY = VAR == VAR_EARLY;
+    static constexpr bool WEAVE = VAR == VAR_WEAVE;
     static constexpr int CPOL = VAR == VAR_NT ? 2 : (VAR == VAR_SC1 ? 16 : (VAR == VAR_SC0 ? 1 : 0));
     static constexpr int RSL = SPLIT ? RS / 2 : RS;   // rows per load round of one loader
     static constexpr int HW = NT / 128;                // wavefronts per operand when split
@@ -293,6 +296,34 @@ struct RingTile {
     // LDS budget, checked at build time (160 KiB per workgroup on gfx950).
     static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
     typedef typename AccOf<P>::type acc_t;
+
+    // WEAVE: instruction order of one scheduling region of NMF MFMAs: the
+    // TM + TN fragment reads two after each of the first MFMAs, then (step 0)
+    // the NL direct-to-LDS loads two after each following MFMA, then the
+    // remaining MFMAs. The masks are the scheduler's instruction classes: 0x8
+    // MFMA, 0x100 LDS read, 0x20 vector-memory read.
+    template <bool WITH_DMA, int NMF>
+    static __device__ __forceinline__ void weave_order() {
+        constexpr int NR = TM + TN;
+        constexpr int RG = (NR + 1) / 2;   // MFMAs that carry the reads
+#pragma unroll
+        for (int i = 0; i < RG; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        if constexpr (WITH_DMA) {
+            constexpr int DG = (NL + 1) / 2;
+            static_assert(RG + DG <= TM * TN, "loads fit between the MFMAs");
+#pragma unroll
+            for (int i = 0; i < DG; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF - RG - DG, 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF - RG, 0);
+        }
+    }
 
     static __device__ __forceinline__ void mainloop(const GemmProblem &p, uint8_t *smem, int row0,
                                                     int col0, int e0, int e1, int tid, int lane,
@@ -413,7 +444,7 @@ struct RingTile {
             const uint8_t *S = smem + (e % NS) * STAGE;
             const uint8_t *Snext = smem + ((e + 1) % NS) * STAGE;
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (!SPREAD && !EARLY)
+            if constexpr (!SPREAD && !EARLY && !WEAVE)
                 dma_entry(e + NS - 1);
 #pragma unroll
             for (int step = 0; step < STEPS - 1; ++step) {
@@ -427,7 +458,7 @@ struct RingTile {
                 // Without it the compiler puts a full LDS wait after those
                 // reads, since it counts the direct-to-LDS loads of step 0 as
                 // LDS accesses that may complete out of order.
-                if constexpr (EARLY)
+                if constexpr (EARLY || WEAVE)
                     if (step > 0)
                         wait_lds_only();
                 if (step % 2 == 0)
@@ -439,10 +470,19 @@ struct RingTile {
                     if (!SPREAD && step == 0)
                         dma_entry(e + NS - 1);   // interleaved with step 0's MFMAs
                 }
+                if constexpr (WEAVE)
+                    if (step == 0)
+                        dma_entry(e + NS - 1);
                 if (step % 2 == 0)
                     mfma_step<P, TM, TN>(fa0, fb0, acc);
                 else
                     mfma_step<P, TM, TN>(fa1, fb1, acc);
+                if constexpr (WEAVE) {
+                    if (step == 0)
+                        weave_order<true, TM * TN>();
+                    else
+                        weave_order<false, TM * TN>();
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (SPREAD)
@@ -457,6 +497,8 @@ struct RingTile {
             if constexpr (EARLY)
                 __builtin_amdgcn_sched_barrier(0);
             mfma_step<P, TM, TN, KA, NMF>(fa1, fb1, acc);
+            if constexpr (WEAVE)
+                weave_order<false, NMF - KA>();
             __builtin_amdgcn_sched_barrier(0);
         }
         // the last entries' dummy loads must land before the ring is reused
@@ -1243,6 +1285,7 @@ static const CfgShape kCfg[CFG_COUNT] = {
     {256, 256, 128, 1, "256x256_bk128_a_ring2_b_direct"},
     {256, 256, 128, 1, "256x256_bk128_ring2_sc0"},
     {256, 256, 128, 1, "256x256_bk128_ring2_early_frag_reads"},
+    {256, 256, 128, 1, "256x256_bk128_ring2_woven_frag_reads"},
 };
 
 const char *tile_cfg_name(int cfg) {
@@ -1404,6 +1447,7 @@ static hipError_t launch_prec(int cfg, const GemmProblem &p, const StreamKPlan &
     case CFG_256x256_DTV: return launch_dtv<P, 2>(p, sk, ws, stream);
     case CFG_256x256_SC0: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_SC0>(p, sk, ws, stream);
     case CFG_256x256_EARLY: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_EARLY>(p, sk, ws, stream);
+    case CFG_256x256_WEAVE: return launch_one<P, 256, 256, 128, 2, 2, 2, VAR_WEAVE>(p, sk, ws, stream);
     default: return hipErrorInvalidValue;
     }
 }

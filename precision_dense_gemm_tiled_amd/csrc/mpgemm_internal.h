@@ -52,6 +52,7 @@ enum TileCfg {
     CFG_256x256_DTV = 18,   // B straight from global memory into MFMA registers, only A through LDS
     CFG_256x256_SC0 = 19,   // (ablation of CFG_256x256_BK128) tile loads with the sc0 cache-policy bit
     CFG_256x256_EARLY = 20, // (ablation of CFG_256x256_BK128) fragment reads fenced ahead of each k-step's MFMAs
+    CFG_256x256_WEAVE = 21, // (ablation of CFG_256x256_BK128) fragment reads woven between a k-step's first MFMAs
     CFG_COUNT
 };
 

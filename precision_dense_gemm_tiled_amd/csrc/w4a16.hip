@@ -576,7 +576,9 @@ template <int MB, int NB, int WN>
 __global__ __launch_bounds__(256) void w4a16_reduce_kernel(W4A16Problem p, W4A16Split sk) {
     constexpr int BM = 16 * MB, BN = 16 * NB * WN, TILE = BM * BN;
     static_assert(TILE % 4 == 0 && (64 * WN) % 4 == 0, "vector groups");
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // the same XCD-contiguous renumbering as the slice kernel, so that the
+    // workgroups adding a tile's slices run on the XCD whose L2 wrote them
+    const int64_t e = (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
     const int64_t tiles = (int64_t)sk.mblocks * sk.ngroups;
     if (e >= tiles * (TILE / 4))
         return;
@@ -1005,26 +1007,32 @@ __global__ __launch_bounds__(256) void w4a16_ring_kernel(W4A16Problem p, W4A16Sp
                         p.Y[(int64_t)m * p.ldy + n] = __builtin_bit_cast(uint16_t, (_Float16)y[e]);
                 }
             } else {
-                const int64_t pn = (int64_t)sk.ngroups * RG_BN;
-                float *dst = sk.partial + ((int64_t)ks * sk.mblocks * RG_BM + m0 + ml) * pn + n;
+                // tile-major slices: tile t's slice ks is one 128 x 64 block
+                float *dst = sk.partial + (((int64_t)tile * sk.ks + ks) * RG_BM + ml) * RG_BN + (n - n0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    dst[e * pn] = y[e];
+                    dst[e * RG_BN] = y[e];
             }
         }
 }
 
-// Y = fp16(sum of the KS row-major fp32 slices written by w4a16_ring_kernel),
-// slices added in slice order; one thread per 4 consecutive columns.
+// Y = fp16(sum of the KS fp32 slices written by w4a16_ring_kernel), slices
+// added in slice order; one thread per 4 consecutive columns of a tile row,
+// 8 workgroups per 128 x 64 tile. Workgroups are renumbered like the ring
+// kernel's, so the ones adding a tile run on the XCD whose L2 holds its
+// slices.
 __global__ __launch_bounds__(256) void w4a16_rowsum_kernel(W4A16Problem p, W4A16Split sk) {
-    const int qpr = (p.N + 3) / 4;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= (int64_t)p.M * qpr)
+    constexpr int TPT = RG_BM * RG_BN / 4;   // threads per tile
+    const int64_t e = (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+    const int tile = (int)(e / TPT), q = (int)(e % TPT);
+    if (tile >= sk.mblocks * sk.ngroups)
         return;
-    const int m = (int)(e / qpr), n = (int)(e % qpr) * 4;
-    const int64_t pn = (int64_t)sk.ngroups * RG_BN;
-    const int64_t slice = (int64_t)sk.mblocks * RG_BM * pn;
-    const f32x4 *src = reinterpret_cast<const f32x4 *>(sk.partial + (int64_t)m * pn + n);
+    const int ml = q / (RG_BN / 4), nl = 4 * (q % (RG_BN / 4));
+    const int m = (tile % sk.mblocks) * RG_BM + ml, n = (tile / sk.mblocks) * RG_BN + nl;
+    if (m >= p.M || n >= p.N)
+        return;
+    const int64_t slice = (int64_t)RG_BM * RG_BN;
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(sk.partial + (int64_t)tile * sk.ks * slice + ml * RG_BN + nl);
     f32x4 y = src[0];
     for (int o = 1; o < sk.ks; ++o)
         y += src[o * (slice / 4)];
@@ -1119,7 +1127,7 @@ static hipError_t launch_ring(const W4A16Problem &p, const W4A16Plan &plan, cons
     hipLaunchKernelGGL((w4a16_ring_kernel<NSTG>), dim3((unsigned)blocks), dim3(256), 0, stream, p, sk, lg);
     if (sk.ks == 1)
         return hipGetLastError();
-    const int64_t threads = (int64_t)p.M * ((p.N + 3) / 4);
+    const int64_t threads = (int64_t)sk.mblocks * sk.ngroups * (RG_BM * RG_BN / 4);
     hipLaunchKernelGGL(w4a16_rowsum_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p, sk);
     return hipGetLastError();
 }
