@@ -56,6 +56,8 @@ def log(*a):
 
 TILE_SOURCE = os.path.join(ROOT, "precision_dense_gemm_tiled_amd", "csrc", "gemm_tile.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_gemm_tile_f16_8192.md")
+W4A16_SOURCE = os.path.join(ROOT, "precision_dense_gemm_tiled_amd", "csrc", "w4a16.hip")
+W4A16_TRACE_PROFILE = os.path.join(ROOT, "profiles", "w4a16_4096_kernel_trace.md")
 
 
 def source_sha256(path):
@@ -76,6 +78,21 @@ def measured_traffic():
     if not sha or not val or sha.group(1) != source_sha256(TILE_SOURCE):
         return None
     return float(val.group(1))
+
+
+def w4a16_kernel_trace():
+    """Per-call kernel durations (ns, summed over the kernels of a call) of
+    the W4A16 workloads from the committed rocprofv3 kernel-trace summary, as
+    {M: ns}, or None if there is none or the kernel source changed since."""
+    try:
+        text = open(W4A16_TRACE_PROFILE).read()
+    except OSError:
+        return None
+    sha = re.search(r"w4a16_source_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"kernel_trace_ns_per_call:\s*(\{.*\})", text)
+    if not sha or not val or sha.group(1) != source_sha256(W4A16_SOURCE):
+        return None
+    return {int(k): float(v) for k, v in json.loads(val.group(1)).items()}
 
 
 def algorithmic_bytes(prec, M, N, K, G=W4A16_G):
@@ -194,6 +211,48 @@ def transpose_b(prec, B, N, K):
     return (qt[:, 0::2] | (qt[:, 1::2] << 4)).astype(np.uint8)
 
 
+class ReadProblem:
+    """A plain streaming read of `nbytes` (mpgemm_stream_read), rotating over
+    enough distinct copies that the Infinity Cache cannot serve repeats: the
+    cold-read ceiling of a call that must move those bytes once."""
+
+    def __init__(self, nbytes, loads_per_lane, copies):
+        import torch
+        self.nbytes = nbytes
+        self.lpl = loads_per_lane
+        base = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+        self.ins = [base] + [base.clone() for _ in range(copies - 1)]
+        self.words = -(-nbytes // (4096 * loads_per_lane))
+        self.out = torch.empty(self.words, dtype=torch.int32, device="cuda")
+        self.i = 0
+
+    def launch(self):
+        import torch
+        import precision_dense_gemm_tiled_amd as mp
+        src = self.ins[self.i % len(self.ins)]
+        self.i += 1
+        st = mp.mpgemm_stream_read(src.data_ptr(), self.nbytes, self.lpl, self.out.data_ptr(), self.words,
+                                   torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise mp.MpgemmError(st, "mpgemm_stream_read")
+
+
+def read_floor(nbytes, steps):
+    """Fastest cold streaming read of nbytes over 1, 2, 4 and 8 loads per
+    lane: (seconds per read, loads per lane)."""
+    import torch
+    copies = int(math.ceil(2 * MALL_BYTES / nbytes))
+    best = None
+    for lpl in (1, 2, 4, 8):
+        p = ReadProblem(nbytes, lpl, copies)
+        t = time_graph(p, max(copies, 2048 // 4), max(steps, 3))
+        del p
+        torch.cuda.empty_cache()
+        if best is None or t < best[0]:
+            best = (t, lpl)
+    return best
+
+
 def copies_for_cold(prec, M, N, K):
     b = algorithmic_bytes(prec, M, N, K)
     return 1 if b >= 2 * MALL_BYTES else int(math.ceil(2 * MALL_BYTES / b))
@@ -301,41 +360,132 @@ def sweep_entry(prec, M, N, K, seed, steps, warmup, eager=False, b_layout="nk", 
     return e
 
 
+def annotate_w4a16(entries, steps):
+    """W4A16 entries gain the cold-read floor of their bytes (the fastest
+    plain streaming read, measured in the same run) and, when the committed
+    kernel-trace summary matches the kernel source, the kernels' own
+    durations per call beside the event-timed figure (which includes the
+    dispatch gaps of the replayed graph)."""
+    trace = w4a16_kernel_trace()
+    for e in entries:
+        nbytes = algorithmic_bytes("w4a16", e["M"], e["N"], e["K"])
+        t_floor, lpl = read_floor(nbytes, steps)
+        e["cold_read_floor_us"] = round(t_floor * 1e6, 3)
+        e["cold_read_floor_GBps"] = round(nbytes / t_floor / 1e9, 1)
+        e["cold_read_floor_loads_per_lane"] = lpl
+        e["us_over_floor"] = round(e["us"] / (t_floor * 1e6), 3)
+        e["roofline_from"] = "hip events around graph replays (dispatch gaps included)"
+        if trace and e["M"] in trace:
+            t_k = trace[e["M"]] * 1e-9
+            e["kernel_trace_us"] = round(t_k * 1e6, 3)
+            e["kernel_trace_roofline_frac"] = roofline("w4a16", e["M"], e["N"], e["K"], t_k)["frac"]
+            e["kernel_trace_over_floor"] = round(t_k / t_floor, 3)
+            e["kernel_trace_source"] = "profiles/w4a16_4096_kernel_trace.md"
+        else:
+            e["kernel_trace_us"] = None
+    return entries
+
+
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(budget_s=15.0):
-    """The CPU oracle (test infrastructure) timed on a bounded row sample of
-    the 8192^3 FP16 problem: all of B against the first r rows of A, r chosen
-    from a short calibration run so the timed call takes about budget_s."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_rows(prec, n, seed, budget_s):
+    """The oracle on the first r rows of an n^3 problem against all of B, r
+    calibrated so the timed call takes about budget_s: (rows, seconds)."""
+    import oracle
+    from precision_dense_gemm_tiled_amd import inputs
+
+    def gen_a(rows):
+        return inputs.gemm_problem(prec, rows, 1, n, seed)[0] if prec != "f16" else \
+            inputs.f16_uniform(seed, 0, rows, n, -1.0, 1.0)
+
+    if prec == "f16":
+        B = inputs.f16_uniform(seed, n * n, n, n, -1.0, 1.0)
+    else:
+        B = inputs.gemm_problem(prec, n, n, n, seed)[1]
+    run = {"f16": lambda a: oracle.gemm_f16(a, B), "i8": lambda a: oracle.gemm_i8(a, B),
+           "i4": lambda a: oracle.gemm_i4(a, B, n)}[prec]
+    run(gen_a(8))                                  # thread pool, page faults
+    t_cal = []
+    for r in (8, 24):
+        a = gen_a(r)
+        t0 = time.perf_counter()
+        run(a)
+        t_cal.append(time.perf_counter() - t0)
+    per_row = max((t_cal[1] - t_cal[0]) / 16, 1e-7)
+    fixed = max(t_cal[0] - 8 * per_row, 0.0)
+    rows = int(max(8, min(n, (budget_s - fixed) / per_row)))
+    a = gen_a(rows)
+    t0 = time.perf_counter()
+    run(a)
+    return rows, time.perf_counter() - t0
+
+
+def cpu_baseline(budget_s=6.0):
+    """The CPU oracle (test infrastructure, untuned) timed on the host cores
+    beside the GPU figures, in the same run. value: the FP16 8192^3 problem on
+    a row sample (all of B against the first r rows of A, r calibrated to
+    about budget_s). per_config: every workload on a bounded sample (INT8 and
+    INT4 8192^3 row samples, W4A16 4096 x 4096 at M = 1, 16, 128 in full),
+    plus single-thread timings at N = 512 (whole problems) and 2048 (row
+    samples) as a per-core figure. GOPS = 2 M N K / t over the part timed."""
     import oracle
     from precision_dense_gemm_tiled_amd import inputs
     if not os.path.exists(oracle._LIB_PATH):
         from oracle import build
         build.build()
+    threads = oracle.threads()
+    per = []
+
+    def entry(name, prec, M, N, K, dt, nthreads, sampled):
+        per.append({"config": name, "prec": prec, "M": M, "N": N, "K": K, "seconds": round(dt, 4),
+                    "GOPS": round(2.0 * M * N * K / dt / 1e9, 3), "threads": nthreads, "sampled": sampled})
+
     n = 8192
-    seed = inputs.config_seed(CONFIG_INDEX["f16"], n)
-    B = inputs.f16_uniform(seed, n * n, n, n, -1.0, 1.0)
-    # two calibration calls separate the fixed cost (decoding all of B) from
-    # the per-row cost
-    t_cal = []
-    oracle.gemm_f16(inputs.f16_uniform(seed, 0, 8, n, -1.0, 1.0), B)   # thread pool, page faults
-    for r in (32, 96):
-        A = inputs.f16_uniform(seed, 0, r, n, -1.0, 1.0)
-        t0 = time.perf_counter()
-        oracle.gemm_f16(A, B)
-        t_cal.append(time.perf_counter() - t0)
-    per_row = max((t_cal[1] - t_cal[0]) / 64, 1e-6)
-    fixed = max(t_cal[0] - 32 * per_row, 0.0)
-    rows = int(max(32, min(n, (budget_s - fixed) / per_row)))
-    A = inputs.f16_uniform(seed, 0, rows, n, -1.0, 1.0)
-    t0 = time.perf_counter()
-    oracle.gemm_f16(A, B)
-    dt = time.perf_counter() - t0
-    value = 2.0 * rows * n * n / dt / 1e12
-    return {"value": round(value, 6), "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+    rows, dt = _oracle_rows("f16", n, inputs.config_seed(CONFIG_INDEX["f16"], n), budget_s)
+    entry(f"fp16 {n}^3", "f16", rows, n, n, dt, threads, f"first {rows} of {n} rows")
+    head = {"value": round(2.0 * rows * n * n / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
             "sample": f"FP16 8192^3 problem: first {rows} rows of A against all of B "
                       f"({rows}x8192x8192, fp64 oracle including the binary16 decode of A and B), "
                       f"{dt:.1f} s"}
+    for prec, budget in (("i8", 2.0), ("i4", 3.0)):
+        rows, dt = _oracle_rows(prec, n, inputs.config_seed(CONFIG_INDEX[prec], n), budget)
+        entry(f"{prec} {n}^3", prec, rows, n, n, dt, threads, f"first {rows} of {n} rows")
+    for m in W4A16_M:
+        X, W, S = inputs.w4a16_problem(m, W4A16_NK, W4A16_NK, W4A16_G, inputs.config_seed(CONFIG_INDEX["w4a16"], m))
+        t0 = time.perf_counter()
+        oracle.gemm_w4a16(X, W, S, W4A16_NK, W4A16_G)
+        entry(f"w4a16 M={m}", "w4a16", m, W4A16_NK, W4A16_NK, time.perf_counter() - t0, threads, "whole problem")
+    # per core: one thread
+    oracle.set_threads(1)
+    try:
+        for prec in ("i8", "f16", "i4"):
+            idx = CONFIG_INDEX["i8_512"] if prec == "i8" else CONFIG_INDEX[prec]
+            A, B = inputs.gemm_problem(prec, 512, 512, 512, inputs.config_seed(idx, 512))
+            t0 = time.perf_counter()
+            {"i8": lambda: oracle.gemm_i8(A, B), "f16": lambda: oracle.gemm_f16(A, B),
+             "i4": lambda: oracle.gemm_i4(A, B, 512)}[prec]()
+            entry(f"{prec} 512^3, one thread", prec, 512, 512, 512, time.perf_counter() - t0, 1, "whole problem")
+        for prec in ("i8", "f16"):
+            rows, dt = _oracle_rows(prec, 2048, inputs.config_seed(CONFIG_INDEX[prec], 2048), 1.0)
+            entry(f"{prec} 2048^3, one thread", prec, rows, 2048, 2048, dt, 1, f"first {rows} of 2048 rows")
+    finally:
+        oracle.set_threads(threads)
+    head["per_config"] = per
+    head["cpu_model"] = cpu_model()
+    head["hardware_concurrency"] = os.cpu_count()
+    head["omp_threads"] = threads
+    return head
 
 
 # ------------------------------------------------------------------ main
@@ -361,6 +511,8 @@ def main():
     ap.add_argument("--launches", type=int, default=None,
                     help="with --only: launches per timed batch (default: enough for ~20 ms); "
                          "counter collection uses a few eager launches")
+    ap.add_argument("--no-floor", action="store_true",
+                    help="with --only w4a16: skip the cold-read floor measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 256 MiB device copy (reference dispatch for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -404,6 +556,8 @@ def main():
                                 args.launches)
                 log(prec, e)
                 out[prec].append(e)
+            if prec == "w4a16" and not args.no_floor:
+                annotate_w4a16(out[prec], args.steps)
         print(json.dumps(out))
         return
 
@@ -448,6 +602,11 @@ def main():
                 log(f"[bench] {prec} {M}x{N}x{K}: {e['us']} us, {e['throughput']} {e['unit']}, "
                     f"{e['roofline_bound']} frac {e['roofline_frac']}{warm}")
                 per[prec].append(e)
+            if prec == "w4a16":
+                annotate_w4a16(per[prec], 5)
+                for e in per[prec]:
+                    log(f"[bench] w4a16 M={e['M']}: cold-read floor {e['cold_read_floor_us']} us, "
+                        f"call {e['us']} us ({e['us_over_floor']}x), kernel trace {e['kernel_trace_us']} us")
         result["per_precision"] = per
 
         # one pass of the whole hot path at the largest sizes

@@ -231,6 +231,20 @@ mpgemm_status_t mpgemm_quantize_w4(mpgemm_handle_t h, int64_t N, int64_t K,
                                    uint8_t *Wq, int64_t ldwq, uint16_t *S, int64_t lds,
                                    void *stream);
 
+/* Measurement aid: a plain streaming read of `bytes` bytes at `src` (device
+ * memory, 16-byte aligned, bytes a multiple of 16) with 16-byte loads,
+ * loads_per_lane (1, 2, 4 or 8) per lane, all issued before any is combined.
+ * Workgroup b writes the XOR of every 32-bit word it read to sink[b]; the
+ * XOR of sink[0 .. blocks) is the XOR of the whole buffer (blocks =
+ * ceil(bytes / (4096 * loads_per_lane)), at most sink_words, else
+ * MPGEMM_ERR_INVALID_ARG). It times the cold read of the bytes a memory-bound
+ * call must move: the attainable ceiling measured on the card ("Warp-
+ * Specialized Kernel Implementation for W4A4 MatMul on Latest GPU
+ * Architectures", section 2: utilisation against a ceiling calibrated on the
+ * same GPU). Asynchronous on `stream`; no handle. */
+mpgemm_status_t mpgemm_stream_read(const void *src, int64_t bytes, int loads_per_lane,
+                                   uint32_t *sink, int64_t sink_words, void *stream);
+
 /* Precision tags of mpgemm_plan_gemm. */
 enum {
     MPGEMM_PREC_F16 = 0,

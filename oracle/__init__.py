@@ -48,6 +48,8 @@ def lib():
         L.oracle_quantize_w4.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_threads.restype = None
         _lib = L
     return _lib
 
@@ -68,6 +70,11 @@ def _rows(a, dtype):
 
 def threads() -> int:
     return lib().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the following oracle calls (timing only)."""
+    lib().oracle_set_threads(int(n))
 
 
 def f16_decode(bits: int) -> float:

@@ -306,3 +306,13 @@ int oracle_threads(void)
     return 1;
 #endif
 }
+
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -113,6 +113,8 @@ int oracle_quantize_w4(int64_t N, int64_t K, const uint16_t *W, int64_t ldw, int
 
 /* Number of OpenMP threads a call uses. */
 int oracle_threads(void);
+/* Threads of the next oracle calls (n > 0; for single-thread timings). */
+void oracle_set_threads(int n);
 
 #ifdef __cplusplus
 }

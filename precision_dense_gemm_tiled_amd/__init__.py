@@ -14,7 +14,7 @@ __all__ = [
     "MpgemmError", "lib", "lib_path",
     "mpgemm_create", "mpgemm_destroy", "mpgemm_status_string",
     "mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_run_w4a4", "mpgemm_quantize_w4",
-    "mpgemm_run_w4a16_noalloc",
+    "mpgemm_run_w4a16_noalloc", "mpgemm_stream_read",
     "mpgemm_run_f16_kn", "mpgemm_run_i8_kn", "mpgemm_run_i4_kn",
     "mpgemm_plan_gemm", "mpgemm_plan_w4a16",
     "Handle", "default_handle", "gemm_f16", "gemm_i8", "gemm_i4", "gemm_w4a16", "gemm_w4a4", "quantize_w4",
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.mpgemm_plan_w4a16.restype = ctypes.c_int
         L.mpgemm_quantize_w4.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
         L.mpgemm_quantize_w4.restype = ctypes.c_int
+        L.mpgemm_stream_read.argtypes = [_vp, _i64, ctypes.c_int, _vp, _i64, _vp]
+        L.mpgemm_stream_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -158,6 +160,10 @@ def mpgemm_plan_w4a16(M, N, K, cu_count=256):
 
 def mpgemm_quantize_w4(h, N, K, W, ldw, group_size, Wq, ldwq, S, lds, stream=None) -> int:
     return lib().mpgemm_quantize_w4(h, N, K, W, ldw, group_size, Wq, ldwq, S, lds, stream)
+
+
+def mpgemm_stream_read(src, nbytes, loads_per_lane, sink, sink_words, stream=None) -> int:
+    return lib().mpgemm_stream_read(src, nbytes, loads_per_lane, sink, sink_words, stream)
 
 
 # ------------------------------------------------------------------ torch helpers

@@ -209,3 +209,16 @@ def test_quantize_argument_errors_without_device(mp, args, expect):
 ])
 def test_w4a4_argument_errors_without_device(mp, args, expect):
     assert mp.mpgemm_run_w4a4(None, *args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A, 4096, 3, C, 4), 2),        # loads per lane not 1, 2, 4 or 8
+    ((A, 4008, 1, C, 4), 2),        # not a multiple of 16 bytes
+    ((A + 8, 4096, 1, C, 4), 2),    # source not 16-byte aligned
+    ((A, 4096 * 8, 1, C, 4), 1),    # more workgroups than sink words
+    ((0, 4096, 1, C, 4), 1),        # NULL source
+    ((A, 4096, 1, 0, 4), 1),        # NULL sink
+    ((A, -16, 1, C, 4), 1),         # negative size
+])
+def test_stream_read_argument_errors_without_device(mp, args, expect):
+    assert mp.mpgemm_stream_read(*args, None) == expect

@@ -92,3 +92,17 @@ def test_transposed_b_operand_by_element(prec, N, K):
             assert nib(bt[k, n // 2], n % 2) == nib(B[n, k // 2], k % 2), (n, k)
     if N % 2:
         assert not np.any(bt[:, -1] >> 4)   # the padding nibble is zero
+
+
+def test_w4a16_trace_guard(tmp_path, monkeypatch):
+    """The committed W4A16 kernel-trace durations are used only while the
+    weight-only kernel source is the one they were taken on."""
+    t = bench.w4a16_kernel_trace()
+    assert t is not None and set(t) == {1, 16, 128} and all(v > 0 for v in t.values())
+    text = open(bench.W4A16_TRACE_PROFILE).read()
+    other = tmp_path / "trace.md"
+    other.write_text(text.replace(bench.source_sha256(bench.W4A16_SOURCE), "0" * 64))
+    monkeypatch.setattr(bench, "W4A16_TRACE_PROFILE", str(other))
+    assert bench.w4a16_kernel_trace() is None
+    monkeypatch.setattr(bench, "W4A16_TRACE_PROFILE", str(tmp_path / "absent.md"))
+    assert bench.w4a16_kernel_trace() is None
