@@ -119,6 +119,7 @@ mpgemm_status_t run_tile(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int6
     p.sx = sx;
     p.sw = sw;
     p.bias = bias;
+    p.c_vec16 = (reinterpret_cast<uintptr_t>(C) % 16 == 0 && ldc % 4 == 0) ? 1 : 0;
     int cfg = h->forced_tile_cfg >= 0 ? h->forced_tile_cfg
                                       : mpg::choose_tile_cfg(prec, M, N, kbytes, h->cu_count);
     const mpg::StreamKPlan sk =
@@ -177,6 +178,7 @@ mpgemm_status_t run_kn(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int64_
     p.N = (int)N;
     p.kbytes = kbytes;
     p.sx = p.sw = p.bias = nullptr;
+    p.c_vec16 = 0;
     hipError_t e = mpg::launch_gemm_kn(prec, p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
 }

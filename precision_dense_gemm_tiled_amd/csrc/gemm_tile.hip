@@ -121,25 +121,29 @@ __device__ __forceinline__ i32x4 load_chunk_bytes(const uint8_t *row, int64_t of
 
 // MFMAs of one k-step (32 bytes of K per row: one chunk per lane group) on
 // fragments already in registers, restricted to the blocks (i, j) whose flat
-// index i * TN + j lies in [LO, HI).
-template <int P, int TM, int TN, int LO = 0, int HI = TM * TN>
+// index i * TN + j lies in [LO, HI). With TRANS the two operands trade
+// places, so each accumulator block holds the transpose of its C block
+// (store_tile_lds reads that layout).
+template <int P, int TM, int TN, int LO = 0, int HI = TM * TN, bool TRANS = false>
 __device__ __forceinline__ void mfma_step(const i32x4 (&a)[TM], const i32x4 (&b)[TN],
                                           typename AccOf<P>::type (&acc)[TM][TN]) {
 #pragma unroll
     for (int f = LO; f < HI; ++f) {
         const int i = f / TN, j = f % TN;
+        const i32x4 x = TRANS ? b[j] : a[i];
+        const i32x4 y = TRANS ? a[i] : b[j];
         if constexpr (P == PREC_I8) {
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(x, y, acc[i][j], 0, 0, 0);
         } else if constexpr (P == PREC_F16) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8, a[i]), __builtin_bit_cast(f16x8, b[j]), acc[i][j], 0, 0, 0);
+                __builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), acc[i][j], 0, 0, 0);
         } else {
             // INT4: widen both operands (16 * nibble per byte) right before use
             const int M4 = (int)0xF0F0F0F0u;
-            const i32x4 ah = a[i] & M4, al = (a[i] << 4) & M4;
-            const i32x4 bh = b[j] & M4, bl = (b[j] << 4) & M4;
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ah, bh, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(al, bl, acc[i][j], 0, 0, 0);
+            const i32x4 xh = x & M4, xl = (x << 4) & M4;
+            const i32x4 yh = y & M4, yl = (y << 4) & M4;
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xh, yh, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xl, yl, acc[i][j], 0, 0, 0);
         }
     }
 }
@@ -199,6 +203,72 @@ __device__ __forceinline__ void store_tile(const GemmProblem &p, int row0, int c
                 }
             }
         }
+}
+
+// Epilogue for transposed accumulators (mfma_step with TRANS): register r
+// of lane l in block (i, j) holds row 32 i + l % 32 and column
+// 32 j + 8 (r / 4) + 4 (l / 32) + r % 4 of the wavefront's WTM x WTN
+// sub-tile, so each group of four registers is four consecutive columns of
+// one row. The wavefront stages RP rows at a time in its own LDS region
+// (row-major, WTN * 4 bytes per row, 16-byte chunk c of row r stored at
+// chunk c ^ (r & 15), which keeps both the writes and the read-back free of
+// bank conflicts), then reads whole row segments back and writes C with
+// 16-byte stores (per-element stores at the right and bottom edges, or when
+// C rows are not 16-byte aligned). Only this wavefront touches its region:
+// no barrier between the passes.
+template <int P, int TM, int TN, int RP>
+__device__ __forceinline__ void store_tile_lds(const GemmProblem &p, uint8_t *region, int row0, int col0,
+                                               int lane, const typename AccOf<P>::type (&acc)[TM][TN]) {
+    typedef typename AccOf<P>::out out_t;
+    typedef out_t out4 __attribute__((ext_vector_type(4)));
+    constexpr int WTN = TN * 32, RB = WTN * 4, CPW = WTN / 4;   // bytes and 16-byte chunks per row
+    static_assert(CPW >= 16 && RP % 32 == 0 && (TM * 32) % RP == 0 && (RP * CPW) % 64 == 0, "staging shape");
+    out_t *C = reinterpret_cast<out_t *>(p.C);
+    const bool vec = p.c_vec16 != 0;
+#pragma unroll
+    for (int pass = 0; pass < TM * 32 / RP; ++pass) {
+#pragma unroll
+        for (int ib = 0; ib < RP / 32; ++ib) {
+            const int i = pass * (RP / 32) + ib;
+            const int rl = ib * 32 + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c = 8 * j + 2 * g + (lane >> 5);
+                    out4 v;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        if constexpr (P == PREC_I4)
+                            v[d] = acc[i][j][4 * g + d] >> 8;
+                        else
+                            v[d] = acc[i][j][4 * g + d];
+                    }
+                    *reinterpret_cast<out4 *>(region + rl * RB + ((c ^ (rl & 15)) * 16)) = v;
+                }
+        }
+#pragma unroll
+        for (int q = 0; q < RP * CPW / 64; ++q) {
+            const int f = q * 64 + lane;
+            const int rl = f / CPW, c = f % CPW;
+            const out4 v = *reinterpret_cast<const out4 *>(region + rl * RB + ((c ^ (rl & 15)) * 16));
+            const int row = row0 + pass * RP + rl, col = col0 + c * 4;
+            if (row < p.M) {
+                out_t *dst = C + (int64_t)row * p.ldc + col;
+                if (vec && col + 3 < p.N) {
+                    // non-temporal: C is written once and never read back
+                    // here, so it should not displace A and B lines that
+                    // later tiles still read from the caches
+                    __builtin_nontemporal_store(v, reinterpret_cast<out4 *>(dst));
+                } else {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        if (col + d < p.N)
+                            dst[d] = v[d];
+                }
+            }
+        }
+    }
 }
 
 // W4A4 epilogue factors of a BM x BN tile staged in LDS as fp32 (the operand
@@ -296,6 +366,14 @@ struct RingTile {
     // LDS budget, checked at build time (160 KiB per workgroup on gfx950).
     static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
     typedef typename AccOf<P>::type acc_t;
+    // Accumulators hold transposed blocks (operands swapped in the MFMA) for
+    // the 4-byte outputs, written back through LDS with 16-byte stores
+    // (store_tile_lds); the W4A4 epilogue keeps the direct layout.
+    static constexpr bool TRANS = P != PREC_W4A4 && WTN >= 64;
+    static constexpr int NW = WGM * WGN;
+    static constexpr int RP_MAX = (LDS_BYTES / NW) / (WTN * 4) / 32 * 32;   // rows one pass can stage
+    static constexpr int RP = RP_MAX >= WTM ? WTM : (WTM % RP_MAX == 0 ? RP_MAX : 32);
+    static_assert(!TRANS || (RP >= 32 && RP * WTN * 4 * NW <= LDS_BYTES), "epilogue staging fits the ring");
 
     // WEAVE: instruction order of one scheduling region of NMF MFMAs: the
     // TM + TN fragment reads two after each of the first MFMAs, then (step 0)
@@ -474,9 +552,9 @@ struct RingTile {
                     if (step == 0)
                         dma_entry(e + NS - 1);
                 if (step % 2 == 0)
-                    mfma_step<P, TM, TN>(fa0, fb0, acc);
+                    mfma_step<P, TM, TN, 0, TM * TN, TRANS>(fa0, fb0, acc);
                 else
-                    mfma_step<P, TM, TN>(fa1, fb1, acc);
+                    mfma_step<P, TM, TN, 0, TM * TN, TRANS>(fa1, fb1, acc);
                 if constexpr (WEAVE) {
                     if (step == 0)
                         weave_order<true, TM * TN>();
@@ -487,7 +565,7 @@ struct RingTile {
             }
             if constexpr (SPREAD)
                 dma_step(e + NS - 1, STEPS - 1);
-            mfma_step<P, TM, TN, 0, KA>(fa1, fb1, acc);
+            mfma_step<P, TM, TN, 0, KA, TRANS>(fa1, fb1, acc);
             __builtin_amdgcn_sched_barrier(0);
             stage_regs(e + NS - 1);   // (VGPR-staged variant only) into the free stage
             wait_vm_lds<(NS - 2) * NL>();
@@ -496,7 +574,7 @@ struct RingTile {
             read_frags<BM, BKB, TM, TN>(Snext, 0, wm0, wn0, lane, fa0, fb0);
             if constexpr (EARLY)
                 __builtin_amdgcn_sched_barrier(0);
-            mfma_step<P, TM, TN, KA, NMF>(fa1, fb1, acc);
+            mfma_step<P, TM, TN, KA, NMF, TRANS>(fa1, fb1, acc);
             if constexpr (WEAVE)
                 weave_order<false, NMF - KA>();
             __builtin_amdgcn_sched_barrier(0);
@@ -505,11 +583,30 @@ struct RingTile {
         wait_vm_lds<0>();
     }
 
-    // Output of a finished tile: C for the plain GEMMs; for W4A4 the scale
-    // epilogue with the factors staged in the (then free) LDS ring.
+    // Output of a finished tile from this loop's accumulators: C through LDS
+    // with 16-byte stores for the transposed layout (every wavefront must be
+    // past its last fragment read and its loads landed before the ring is
+    // reused: one barrier), otherwise as epilogue_direct.
     static __device__ __forceinline__ void epilogue(const GemmProblem &p, uint8_t *smem, int row0,
                                                     int col0, int tid, int lane, int wave,
                                                     const acc_t (&acc)[TM][TN]) {
+        if constexpr (TRANS) {
+            const int wm0 = (wave / WGN) * WTM;
+            const int wn0 = (wave % WGN) * WTN;
+            __syncthreads();
+            store_tile_lds<P, TM, TN, RP>(p, smem + wave * (LDS_BYTES / NW), row0 + wm0, col0 + wn0, lane,
+                                          acc);
+        } else {
+            epilogue_direct(p, smem, row0, col0, tid, lane, wave, acc);
+        }
+    }
+
+    // Output of a finished tile whose accumulators hold C blocks directly
+    // (not transposed): C for the plain GEMMs; for W4A4 the scale epilogue
+    // with the factors staged in the (then free) LDS ring.
+    static __device__ __forceinline__ void epilogue_direct(const GemmProblem &p, uint8_t *smem, int row0,
+                                                           int col0, int tid, int lane, int wave,
+                                                           const acc_t (&acc)[TM][TN]) {
         const int wm0 = (wave / WGN) * WTM;
         const int wn0 = (wave % WGN) * WTN;
         if constexpr (P == PREC_W4A4) {
@@ -753,7 +850,7 @@ struct DtvTile {
 template <int P, int NS>
 __global__ __launch_bounds__(256) void gemm_dtv_kernel(GemmProblem p, int tiles_m, int tiles_n) {
     typedef DtvTile<P, NS> DT;
-    typedef RingTile<P, 256, 256, 128, 2, 2, 2> RT;   // same wavefront tiles: its epilogue
+    typedef RingTile<P, 256, 256, 128, 2, 2, 2> RT;   // same wavefront tiles: its direct epilogue
     static_assert(RT::LDS_BYTES >= (256 + 2 * 256) * 4, "epilogue staging");
     __shared__ __attribute__((aligned(16))) uint8_t smem[DT::LDS_BYTES];
 
@@ -766,7 +863,7 @@ __global__ __launch_bounds__(256) void gemm_dtv_kernel(GemmProblem p, int tiles_
 
     typename DT::acc_t acc[DT::TM][DT::TN];
     DT::mainloop(p, smem, row0, col0, tid, lane, wave, acc);
-    RT::epilogue(p, smem, row0, col0, tid, lane, wave, acc);
+    RT::epilogue_direct(p, smem, row0, col0, tid, lane, wave, acc);
 }
 
 // Ping-pong kernel for the 256 x 256 tile (data-parallel, K a multiple of

@@ -25,6 +25,9 @@ struct GemmProblem {
     // PREC_W4A4 epilogue: C[m][n] = fp16(acc * sx[m] * sw[n] + bias[n]) (fp16
     // bits; bias may be null); unused by the other precisions
     const uint16_t *sx, *sw, *bias;
+    // 1 when C and every C row start on a 16-byte boundary (the tile epilogue
+    // may then store four consecutive 4-byte outputs at once)
+    int c_vec16;
 };
 
 // Tile configurations of the square/rectangular tile kernel. The index is
