@@ -25,6 +25,18 @@ __device__ __forceinline__ void wait_vm_lds() {
     __builtin_amdgcn_s_waitcnt(imm);
 }
 
+// wait_vm_lds for a count known only after loop unrolling (n folds to a
+// constant there, and the recursion to the one matching wait).
+template <int N = 63>
+__device__ __forceinline__ void wait_vm_lds_n(int n) {
+    if constexpr (N >= 0) {
+        if (n == N)
+            wait_vm_lds<N>();
+        else
+            wait_vm_lds_n<N - 1>(n);
+    }
+}
+
 // s_waitcnt for "all LDS operations done", vector-memory loads left in
 // flight (vmcnt at its maximum).
 __device__ __forceinline__ void wait_lds_only() {

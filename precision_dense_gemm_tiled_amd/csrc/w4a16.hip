@@ -418,16 +418,30 @@ __device__ __forceinline__ int xcd_contiguous(int id, int nblk) {
 }
 
 
-template <int MB, int NB, int WN, int WK, int NST>
+template <int MB, int NB, int WN, int WK, int NST, int PDT>
 __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16Split sk, int lg) {
     static_assert(WN * WK == 4, "4 wavefronts");
     constexpr int BM = 16 * MB, BN = 16 * NB * WN;
-    constexpr int CPROW = 16 * NST * WK;        // 16-byte chunks per LDS row (the workgroup's K range)
-    constexpr int UPR = CPROW / 64;             // 1 KiB direct-to-LDS units per row
-    constexpr int UNITS = BM * UPR;
-    constexpr int NW = NST * NB * 2;            // weight + scale loads per thread
-    static_assert(CPROW % 64 == 0 && UNITS % 4 == 0 && NW < 64, "slice shape");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+    // LDS: the workgroup's NST * WK blocks of 128 k, block-major. Block b
+    // holds two halves of 64 k (BM rows of 128 bytes each); row r's 16-byte
+    // chunk c of a half sits at slot c ^ ((r / 2) & 7). MFMA lane group g
+    // takes the 32-k quarter pi(g) = 0, 2, 1, 3 (g = 0..3) of each 128 k, for
+    // the weights and the activations alike, so that lanes l and l + 16 read
+    // the same slot of the same row in the two halves (BM * 128 bytes apart,
+    // the same 16-byte bank group), and lanes 0-15 read 16 rows at 16
+    // distinct bank groups: the fragment reads are free of bank conflicts. A
+    // direct-to-LDS unit (1 KiB) is 8 whole rows of one half: every 128-byte
+    // line of X is fetched once.
+    constexpr int PB = BM * 128, BLOCK = 2 * PB;   // bytes per half, per block
+    constexpr int NBLK = NST * WK;
+    constexpr int XU = WK * MB;                  // direct-to-LDS loads per wavefront per step
+    constexpr int WL = 2 * NB;                   // weight + scale loads per wavefront per step
+    constexpr int PD = PDT < NST ? PDT : NST;    // steps of loads in flight ahead of the products
+    static_assert((PD - 1) * (XU + WL) < 64 && NST * WL < 64, "vmcnt of the step waits");
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
+    // explicitly uniform: the direct-to-LDS destinations derived from it
+    // then live in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % WN, wk = wave / WN;
 
     // Workgroup -> (column group, row block, K slice). Consecutive workgroup
@@ -442,25 +456,8 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
     const int k_end = min(p.K, k_begin + sk.kslice);
     const int kw = k_begin + wk * 128 * NST;    // this wavefront's K range starts here
     const int n0w = ng * BN + wn * 16 * NB;
+    __shared__ __attribute__((aligned(16))) uint8_t xs[NBLK * BLOCK];
 
-    // 1. activation rows of the workgroup's K range -> LDS (clamped addresses:
-    //    rows past M and k past the range only meet zero weights or outputs
-    //    that are never stored)
-    __shared__ __attribute__((aligned(16))) uint8_t xs[BM * CPROW * 16];
-#pragma unroll
-    for (int v = 0; v < UNITS / 4; ++v) {
-        const int u = wave + 4 * v, r = u / UPR, p0 = (u % UPR) * 64;
-        const int c = (p0 + lane) ^ (r & 15);
-        const int k = min(k_begin + 8 * c, p.K - 8);
-        const uint16_t *src = p.X + (int64_t)min(m0 + r, p.M - 1) * p.ldx + k;
-        dma16(src, xs + (r * CPROW + p0) * 16);
-    }
-    // the weight loads below must stay behind the direct-to-LDS loads: the
-    // wait before the first fragment read counts on the NW youngest loads
-    // being theirs
-    asm volatile("" ::: "memory");
-
-    // 2. every weight word and scale of this wavefront's K range -> registers
     const uint8_t *wrow[NB];
     const uint16_t *srow[NB];
 #pragma unroll
@@ -469,41 +466,102 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
         wrow[j] = p.W + (int64_t)n * p.ldw_b;
         srow[j] = p.S + (int64_t)n * p.lds;
     }
+    // lane l of an activation unit (8 rows of one half) covers row
+    // 8 q + l / 8 and chunk c = (l % 8) ^ ((row / 2) % 8) of its slot l % 8
+    const int pig = ((g & 1) << 1) | (g >> 1);   // this lane group's quarter
+    const uint16_t *xrow[XU];
+    int xc8[XU];
+#pragma unroll
+    for (int v = 0; v < XU; ++v) {
+        const int q = (wave + 4 * v) % (2 * MB);
+        const int r = 8 * q + (lane >> 3);
+        xrow[v] = p.X + (int64_t)min(m0 + r, p.M - 1) * p.ldx;
+        xc8[v] = 8 * ((lane & 7) ^ ((r >> 1) & 7));
+    }
     i32x4 wr[NST][NB];
     uint16_t sr[NST][NB];
+    // Loads of step s: block wk' * NST + s of every wavefront group wk'
+    // (activations, direct to LDS, shared by the workgroup) and this
+    // wavefront's weights and scales of its block s. Clamped addresses: rows
+    // past M and k past the range only meet zero weights or outputs that are
+    // never stored.
+    auto issue_x = [&](int s) {
 #pragma unroll
-    for (int s = 0; s < NST; ++s) {
-        int k = kw + 128 * s + 32 * g;
+        for (int v = 0; v < XU; ++v) {
+            const int u = wave + 4 * v;                 // unit of this step: (block group, half, rows)
+            const int b = (u / (4 * MB)) * NST + s;     // block
+            const int h = (u / (2 * MB)) % 2, q = u % (2 * MB);   // half, 8-row group
+            const int k = min(k_begin + 128 * b + 64 * h + xc8[v], p.K - 8);
+            dma16(xrow[v] + k, xs + b * BLOCK + h * PB + q * 1024);
+        }
+        asm volatile("" ::: "memory");
+    };
+    auto issue_w = [&](int s) {
+        int k = kw + 128 * s + 32 * pig;
         k = k + 32 <= p.K ? k : p.K - 32;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             wr[s][j] = *reinterpret_cast<const i32x4 *>(wrow[j] + (k >> 1));
             sr[s][j] = srow[j][k >> lg];
         }
+        asm volatile("" ::: "memory");
+    };
+    // PD < NST: step by step (activations, then weights, of each step);
+    // PD = NST: every activation load first, then the weights, so that the
+    // products can start once the activations alone have landed
+#pragma unroll
+    for (int s = 0; s < PD; ++s) {
+        issue_x(s);
+        if constexpr (PD < NST)
+            issue_w(s);
     }
-    wait_vm_lds<NW>();
-    lds_barrier();
+    if constexpr (PD == NST) {
+#pragma unroll
+        for (int s = 0; s < NST; ++s)
+            issue_w(s);
+    }
 
-    // 3. products, no barrier: the weights of step s arrive in issue order
+    // products step by step; each step first waits for its own loads (the
+    // younger ones are the next steps', at most PD - 1 of them), then puts
+    // the loads of step s + PD in flight
     f32x4 acc[MB][NB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const i32x4 *xq = reinterpret_cast<const i32x4 *>(xs);
+    // per-lane part of the fragment address of MFMA step t: quarter pi(g)
+    // (half pi(g) / 2, chunks 4 (pi(g) % 2) + t), row 16 i + l % 16 (16 i
+    // does not change the swizzle bits)
+    int aoff[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int r = lane & 15;
+        aoff[t] = (pig >> 1) * PB + r * 128 + (((4 * (pig & 1) + t) ^ ((r >> 1) & 7)) * 16);
+    }
 #pragma unroll
     for (int s = 0; s < NST; ++s) {
+        if (PD < NST || s == 0) {
+            // with every step issued up front (PD = NST) one wait covers all
+            // activations: the younger loads are all the weights
+            const int younger = (s + PD <= NST ? PD : NST - s) - 1;
+            wait_vm_lds_n(PD < NST ? younger * (XU + WL) : NST * WL);
+            lds_barrier();
+        }
+        if (s + PD < NST) {
+            issue_x(s + PD);
+            issue_w(s + PD);
+        }
         if (kw + 128 * s >= k_end)
-            break;
-        const bool live = kw + 128 * s + 32 * g < k_end;
-        const int cs = 16 * (wk * NST + s);
+            continue;   // (the barriers above stay uniform across the wavefronts)
+        const bool live = kw + 128 * s + 32 * pig < k_end;
+        const uint8_t *blk = xs + (wk * NST + s) * BLOCK;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             f16x8 a[MB];
 #pragma unroll
             for (int i = 0; i < MB; ++i)
-                a[i] = __builtin_bit_cast(f16x8, xq[(16 * i + (lane & 15)) * CPROW + cs + ((4 * g + t) ^ (lane & 15))]);
+                a[i] = *reinterpret_cast<const f16x8 *>(blk + aoff[t] + i * 2048);
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 // a run past the K range gets q = 0 (u = 8 in every nibble)
@@ -519,7 +577,7 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
 
     // 4. add the WK partial sums through LDS (reusing the activation buffer)
     if constexpr (WK > 1) {
-        static_assert(BM * CPROW * 16 >= 4 * MB * NB * 4 * 64 * 4, "reduction buffer");
+        static_assert(NBLK * BLOCK >= 4 * MB * NB * 4 * 64 * 4, "reduction buffer");
         __syncthreads();
         f32x4 *red = reinterpret_cast<f32x4 *>(xs);
 #pragma unroll
@@ -1081,7 +1139,7 @@ static hipError_t launch_gemv(const W4A16Problem &p, hipStream_t stream, int lg)
     return launch_gemv_mm<R, KS, 4>(p, stream, lg);
 }
 
-template <int MB, int NB, int WN, int WK, int NST>
+template <int MB, int NB, int WN, int WK, int NST, int PD>
 static hipError_t launch_slice(const W4A16Problem &p, const W4A16Plan &plan, const W4A16Workspace &ws,
                                hipStream_t stream, int lg) {
     constexpr int BM = 16 * MB, BN = 16 * NB * WN;
@@ -1095,7 +1153,7 @@ static hipError_t launch_slice(const W4A16Problem &p, const W4A16Plan &plan, con
     const int64_t blocks = tiles * sk.ks;
     if (blocks > INT_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((w4a16_slice_kernel<MB, NB, WN, WK, NST>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((w4a16_slice_kernel<MB, NB, WN, WK, NST, PD>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        p, sk, lg);
     if (sk.ks == 1)
         return hipGetLastError();
@@ -1134,18 +1192,20 @@ static hipError_t launch_ring(const W4A16Problem &p, const W4A16Plan &plan, cons
 
 // The slice configurations: (configuration, MB, NB, WN, WK, NST). One list
 // feeds both the host planning and the kernel dispatch.
-#define MPG_SLICE_CONFIGS(X)                 \
-    X(W4A16_SLICE_16x16_K4, 1, 1, 1, 4, 8)   \
-    X(W4A16_SLICE_32x32_K2, 2, 1, 2, 2, 8)   \
-    X(W4A16_SLICE_64x128, 4, 2, 4, 1, 8)     \
-    X(W4A16_SLICE_128x128, 8, 2, 4, 1, 4)   \
-    X(W4A16_SLICE_64x128_S4, 4, 2, 4, 1, 4)
+// (config, MB, NB, WN, WK, NST, PD): tile 16 MB x 16 NB WN, WK wavefronts
+// along K, NST steps of 128 k per wavefront, loads PD steps ahead
+#define MPG_SLICE_CONFIGS(X)                    \
+    X(W4A16_SLICE_16x16_K4, 1, 1, 1, 4, 8, 8)   \
+    X(W4A16_SLICE_32x32_K2, 2, 1, 2, 2, 8, 2)   \
+    X(W4A16_SLICE_64x128, 4, 2, 4, 1, 8, 2)     \
+    X(W4A16_SLICE_128x128, 8, 2, 4, 1, 4, 2)    \
+    X(W4A16_SLICE_64x128_S4, 4, 2, 4, 1, 4, 2)
 
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cfg, int cu_count, int64_t partial_floats) {
     W4A16Plan plan{K == 0 ? (int)W4A16_GEMV_R2_KS2 : cfg, 1, 0, 0, 0};
     int MB = 0, NB = 0, WN = 0, WK = 0, NST = 0;
     switch (plan.cfg) {
-#define MPG_SHAPE(C, mb, nb, wn, wk, nst) \
+#define MPG_SHAPE(C, mb, nb, wn, wk, nst, pd) \
     case C: MB = mb; NB = nb; WN = wn; WK = wk; NST = nst; break;
         MPG_SLICE_CONFIGS(MPG_SHAPE)
 #undef MPG_SHAPE
@@ -1203,7 +1263,7 @@ int64_t w4a16_plan_scratch_floats(const W4A16Plan &plan) {
     if (plan.ks <= 1)
         return 0;
     switch (plan.cfg) {
-#define MPG_SCRATCH(C, mb, nb, wn, wk, nst) \
+#define MPG_SCRATCH(C, mb, nb, wn, wk, nst, pd) \
     case C: return (int64_t)plan.ks * plan.mblocks * plan.ngroups * (16 * mb) * (16 * nb * wn);
         MPG_SLICE_CONFIGS(MPG_SCRATCH)
 #undef MPG_SCRATCH
@@ -1227,11 +1287,10 @@ const char *w4a16_cfg_name(int cfg) {
 int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K) {
     (void)N;
     (void)K;
-    // measured at N = K = 4096 (cold weights, HIP graph replay): above 64
-    // rows the ring kernel wins (M = 80: 17.1 vs 18.5 us for the 64 x 128
-    // slices, M = 112: 18.1 vs 18.6; 29 vs 66 at 512, 54 vs 283 at 1024),
-    // except at M = 128, where the slices fill both their row blocks and the
-    // two tie (18.6 vs 18.7 us)
+    // measured at N = K = 4096 (cold weights, HIP graph replay): from 65 to
+    // 128 rows the 64 x 128 slices win (M = 80: 12.6 vs 14.9 us for the ring
+    // kernel, M = 128: 12.7 vs 15.0), above 128 the ring kernel (M = 160: 19.5
+    // vs 20.4 us, 256: 20.0 vs 22.7; 512: 27.4 vs 45.0)
     if (M == 1)
         return W4A16_GEMV_R2_KS2;
     if (M <= 4)
@@ -1244,7 +1303,7 @@ int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K) {
     // per compute unit (M = 48 and 64: 10.6 vs 13.4 us for the 32 x 32 slices)
     if (M <= 64)
         return W4A16_SLICE_64x128_S4;
-    if (M == 128)
+    if (M <= 128)
         return W4A16_SLICE_64x128;
     return W4A16_RING3_128x64;
 }
@@ -1260,8 +1319,8 @@ static hipError_t launch_one(const W4A16Problem &p, const W4A16Plan &plan, const
     case W4A16_GEMV_R2_KS1: return launch_gemv<2, 1>(p, stream, lg);
     case W4A16_GEMV_R4_KS1: return launch_gemv<4, 1>(p, stream, lg);
     case W4A16_GEMV_R8_KS1: return launch_gemv<8, 1>(p, stream, lg);
-#define MPG_LAUNCH(C, mb, nb, wn, wk, nst) \
-    case C: return launch_slice<mb, nb, wn, wk, nst>(p, plan, ws, stream, lg);
+#define MPG_LAUNCH(C, mb, nb, wn, wk, nst, pd) \
+    case C: return launch_slice<mb, nb, wn, wk, nst, pd>(p, plan, ws, stream, lg);
         MPG_SLICE_CONFIGS(MPG_LAUNCH)
 #undef MPG_LAUNCH
     case W4A16_RING3_128x64: return launch_ring<3>(p, plan, ws, stream, lg);
