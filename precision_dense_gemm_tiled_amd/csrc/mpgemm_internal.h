@@ -130,6 +130,7 @@ enum W4A16Cfg {
     W4A16_RING3_128x64 = 12,   // MFMA, 128 x 64 tile, activations and weights through a 3-stage LDS ring
     W4A16_RING4_128x64 = 13,   // ... 4-stage ring
     W4A16_SLICE_64x128_S4 = 14, // slice 64 x 128 over 4 stages of K (64 KiB LDS: two workgroups per CU)
+    W4A16_SLICE_128x64_RING = 15, // slice 128 x 64 over 8 stages of K, activations through a 3-slot LDS ring
     W4A16_CFG_COUNT
 };
 

@@ -366,14 +366,13 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(W4A16Problem p, int lg)
 //
 // Mid-size and prefill M. The weights dominate the bytes and the activations
 // are reused by every output column, so a workgroup keeps the activations of
-// its K range (BM rows) resident in LDS, loaded once with coalesced
-// direct-to-LDS loads into rows whose 16-byte chunks are XOR-swizzled by
-// row & 15 (the 16 rows of a fragment read fall in distinct banks). Its
-// wavefronts stream their weight rows straight into registers, every weight
-// load issued before the first product, dequantise them exactly, multiply by
-// the group scale in fp16 and feed v_mfma_f32_16x16x32_f16 (the
-// fused-int4-gemm-sm75 README dequantises to fp16 in registers before the
-// matrix product).
+// its K range (BM rows) in LDS (resident, or streamed through a few slots),
+// loaded with direct-to-LDS loads in the conflict-free layout described at
+// the kernel. Its wavefronts stream their weight rows straight into
+// registers, a fixed number of 128-k steps ahead of the products, dequantise
+// them exactly, multiply by the group scale in fp16 and feed
+// v_mfma_f32_16x16x32_f16 (the fused-int4-gemm-sm75 README dequantises to
+// fp16 in registers before the matrix product).
 //
 // Dequantisation in natural k order, so the activations need no reordering
 // (dequant8_perm below): with u = nibble ^ 8 = q + 8, the fp16 patterns 0x6400
@@ -418,7 +417,7 @@ __device__ __forceinline__ int xcd_contiguous(int id, int nblk) {
 }
 
 
-template <int MB, int NB, int WN, int WK, int NST, int PDT>
+template <int MB, int NB, int WN, int WK, int NST, int PDT, int RG>
 __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16Split sk, int lg) {
     static_assert(WN * WK == 4, "4 wavefronts");
     constexpr int BM = 16 * MB, BN = 16 * NB * WN;
@@ -438,6 +437,12 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
     constexpr int WL = 2 * NB;                   // weight + scale loads per wavefront per step
     constexpr int PD = PDT < NST ? PDT : NST;    // steps of loads in flight ahead of the products
     static_assert((PD - 1) * (XU + WL) < 64 && NST * WL < 64, "vmcnt of the step waits");
+    // RG > 0: the blocks stream through RG LDS slots (block b in slot b % RG)
+    // instead of all staying resident; the loads of step s + PD go out after
+    // the barrier of step s, when every wavefront is done with step s - 1, so
+    // RG = PD + 1 slots suffice
+    static_assert(RG == 0 || (WK == 1 && PD < NST && RG >= PD + 1), "activation ring");
+    constexpr int NSLOT = RG > 0 ? RG : NBLK;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
     // explicitly uniform: the direct-to-LDS destinations derived from it
     // then live in scalar registers
@@ -456,7 +461,7 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
     const int k_end = min(p.K, k_begin + sk.kslice);
     const int kw = k_begin + wk * 128 * NST;    // this wavefront's K range starts here
     const int n0w = ng * BN + wn * 16 * NB;
-    __shared__ __attribute__((aligned(16))) uint8_t xs[NBLK * BLOCK];
+    __shared__ __attribute__((aligned(16))) uint8_t xs[NSLOT * BLOCK];
 
     const uint8_t *wrow[NB];
     const uint16_t *srow[NB];
@@ -492,7 +497,7 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
             const int b = (u / (4 * MB)) * NST + s;     // block
             const int h = (u / (2 * MB)) % 2, q = u % (2 * MB);   // half, 8-row group
             const int k = min(k_begin + 128 * b + 64 * h + xc8[v], p.K - 8);
-            dma16(xrow[v] + k, xs + b * BLOCK + h * PB + q * 1024);
+            dma16(xrow[v] + k, xs + (RG > 0 ? b % RG : b) * BLOCK + h * PB + q * 1024);
         }
         asm volatile("" ::: "memory");
     };
@@ -555,7 +560,7 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
         if (kw + 128 * s >= k_end)
             continue;   // (the barriers above stay uniform across the wavefronts)
         const bool live = kw + 128 * s + 32 * pig < k_end;
-        const uint8_t *blk = xs + (wk * NST + s) * BLOCK;
+        const uint8_t *blk = xs + (RG > 0 ? (wk * NST + s) % RG : wk * NST + s) * BLOCK;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             f16x8 a[MB];
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
 
     // 4. add the WK partial sums through LDS (reusing the activation buffer)
     if constexpr (WK > 1) {
-        static_assert(NBLK * BLOCK >= 4 * MB * NB * 4 * 64 * 4, "reduction buffer");
+        static_assert(NSLOT * BLOCK >= 4 * MB * NB * 4 * 64 * 4, "reduction buffer");
         __syncthreads();
         f32x4 *red = reinterpret_cast<f32x4 *>(xs);
 #pragma unroll
@@ -1139,7 +1144,7 @@ static hipError_t launch_gemv(const W4A16Problem &p, hipStream_t stream, int lg)
     return launch_gemv_mm<R, KS, 4>(p, stream, lg);
 }
 
-template <int MB, int NB, int WN, int WK, int NST, int PD>
+template <int MB, int NB, int WN, int WK, int NST, int PD, int RG>
 static hipError_t launch_slice(const W4A16Problem &p, const W4A16Plan &plan, const W4A16Workspace &ws,
                                hipStream_t stream, int lg) {
     constexpr int BM = 16 * MB, BN = 16 * NB * WN;
@@ -1153,7 +1158,7 @@ static hipError_t launch_slice(const W4A16Problem &p, const W4A16Plan &plan, con
     const int64_t blocks = tiles * sk.ks;
     if (blocks > INT_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((w4a16_slice_kernel<MB, NB, WN, WK, NST, PD>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((w4a16_slice_kernel<MB, NB, WN, WK, NST, PD, RG>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        p, sk, lg);
     if (sk.ks == 1)
         return hipGetLastError();
@@ -1192,20 +1197,22 @@ static hipError_t launch_ring(const W4A16Problem &p, const W4A16Plan &plan, cons
 
 // The slice configurations: (configuration, MB, NB, WN, WK, NST). One list
 // feeds both the host planning and the kernel dispatch.
-// (config, MB, NB, WN, WK, NST, PD): tile 16 MB x 16 NB WN, WK wavefronts
-// along K, NST steps of 128 k per wavefront, loads PD steps ahead
-#define MPG_SLICE_CONFIGS(X)                    \
-    X(W4A16_SLICE_16x16_K4, 1, 1, 1, 4, 8, 8)   \
-    X(W4A16_SLICE_32x32_K2, 2, 1, 2, 2, 8, 2)   \
-    X(W4A16_SLICE_64x128, 4, 2, 4, 1, 8, 2)     \
-    X(W4A16_SLICE_128x128, 8, 2, 4, 1, 4, 2)    \
-    X(W4A16_SLICE_64x128_S4, 4, 2, 4, 1, 4, 2)
+// (config, MB, NB, WN, WK, NST, PD, RG): tile 16 MB x 16 NB WN, WK
+// wavefronts along K, NST steps of 128 k per wavefront, loads PD steps
+// ahead, activations resident (RG = 0) or through an RG-slot ring
+#define MPG_SLICE_CONFIGS(X)                       \
+    X(W4A16_SLICE_16x16_K4, 1, 1, 1, 4, 8, 8, 0)   \
+    X(W4A16_SLICE_32x32_K2, 2, 1, 2, 2, 8, 2, 0)   \
+    X(W4A16_SLICE_64x128, 4, 2, 4, 1, 8, 2, 0)     \
+    X(W4A16_SLICE_128x128, 8, 2, 4, 1, 4, 2, 0)    \
+    X(W4A16_SLICE_64x128_S4, 4, 2, 4, 1, 4, 2, 0)  \
+    X(W4A16_SLICE_128x64_RING, 8, 1, 4, 1, 8, 2, 3)
 
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cfg, int cu_count, int64_t partial_floats) {
     W4A16Plan plan{K == 0 ? (int)W4A16_GEMV_R2_KS2 : cfg, 1, 0, 0, 0};
     int MB = 0, NB = 0, WN = 0, WK = 0, NST = 0;
     switch (plan.cfg) {
-#define MPG_SHAPE(C, mb, nb, wn, wk, nst, pd) \
+#define MPG_SHAPE(C, mb, nb, wn, wk, nst, pd, rg) \
     case C: MB = mb; NB = nb; WN = wn; WK = wk; NST = nst; break;
         MPG_SLICE_CONFIGS(MPG_SHAPE)
 #undef MPG_SHAPE
@@ -1263,7 +1270,7 @@ int64_t w4a16_plan_scratch_floats(const W4A16Plan &plan) {
     if (plan.ks <= 1)
         return 0;
     switch (plan.cfg) {
-#define MPG_SCRATCH(C, mb, nb, wn, wk, nst, pd) \
+#define MPG_SCRATCH(C, mb, nb, wn, wk, nst, pd, rg) \
     case C: return (int64_t)plan.ks * plan.mblocks * plan.ngroups * (16 * mb) * (16 * nb * wn);
         MPG_SLICE_CONFIGS(MPG_SCRATCH)
 #undef MPG_SCRATCH
@@ -1280,7 +1287,8 @@ const char *w4a16_cfg_name(int cfg) {
         "gemv R1 KS2", "gemv R2 KS2", "gemv R4 KS2", "gemv R2 KS1", "gemv R4 KS1", "gemv R8 KS1",
         "slice 16 x 16, K over 4 wavefronts", "slice 32 x 32, K over 2 wavefronts",
         "slice 64 x 128", "slice 128 x 128", "ring 128 x 64, 3 stages", "ring 128 x 64, 4 stages",
-        "slice 64 x 128, 4 stages (two workgroups per compute unit)"};
+        "slice 64 x 128, 4 stages (two workgroups per compute unit)",
+        "slice 128 x 64, 8 stages through a 3-slot activation ring"};
     return cfg >= 0 && cfg < W4A16_CFG_COUNT ? names[cfg] : "?";
 }
 
@@ -1319,8 +1327,8 @@ static hipError_t launch_one(const W4A16Problem &p, const W4A16Plan &plan, const
     case W4A16_GEMV_R2_KS1: return launch_gemv<2, 1>(p, stream, lg);
     case W4A16_GEMV_R4_KS1: return launch_gemv<4, 1>(p, stream, lg);
     case W4A16_GEMV_R8_KS1: return launch_gemv<8, 1>(p, stream, lg);
-#define MPG_LAUNCH(C, mb, nb, wn, wk, nst, pd) \
-    case C: return launch_slice<mb, nb, wn, wk, nst, pd>(p, plan, ws, stream, lg);
+#define MPG_LAUNCH(C, mb, nb, wn, wk, nst, pd, rg) \
+    case C: return launch_slice<mb, nb, wn, wk, nst, pd, rg>(p, plan, ws, stream, lg);
         MPG_SLICE_CONFIGS(MPG_LAUNCH)
 #undef MPG_LAUNCH
     case W4A16_RING3_128x64: return launch_ring<3>(p, plan, ws, stream, lg);
