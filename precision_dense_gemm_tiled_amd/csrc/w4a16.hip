@@ -219,16 +219,17 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 // Activation chunk (32 fp16, k order) -> pairs (k, k+4) of each 8-k word,
-// in the order the weight pairs are produced.
+// in the order the weight pairs are produced: one byte permute per pair
+// (v_perm_b32: selector bytes 0-3 pick the second source, 4-7 the first).
 __device__ __forceinline__ void pair_x(const i32x4 (&xv)[4], uint32_t (&xp)[16]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const uint32_t d0 = (uint32_t)xv[t][0], d1 = (uint32_t)xv[t][1];
         const uint32_t d2 = (uint32_t)xv[t][2], d3 = (uint32_t)xv[t][3];
-        xp[4 * t + 0] = (d0 & 0xFFFFu) | (d2 << 16);          // k0, k4
-        xp[4 * t + 1] = (d0 >> 16) | (d2 & 0xFFFF0000u);      // k1, k5
-        xp[4 * t + 2] = (d1 & 0xFFFFu) | (d3 << 16);          // k2, k6
-        xp[4 * t + 3] = (d1 >> 16) | (d3 & 0xFFFF0000u);      // k3, k7
+        xp[4 * t + 0] = __builtin_amdgcn_perm(d2, d0, 0x05040100u);   // k0, k4
+        xp[4 * t + 1] = __builtin_amdgcn_perm(d2, d0, 0x07060302u);   // k1, k5
+        xp[4 * t + 2] = __builtin_amdgcn_perm(d3, d1, 0x05040100u);   // k2, k6
+        xp[4 * t + 3] = __builtin_amdgcn_perm(d3, d1, 0x07060302u);   // k3, k7
     }
 }
 
@@ -247,17 +248,30 @@ __device__ __forceinline__ float offset_of_chunk(const uint32_t (&xp)[16]) {
     return a[0] + a[1];
 }
 
-__device__ __forceinline__ float dot_chunk(const i32x4 w, const uint32_t (&xp)[16]) {
+// Masks and exponent patterns of the mask-or steps, held in VGPRs: gfx9's
+// three-operand encoding takes no literal constant, so with literals each
+// mask-or would split into an AND and an OR.
+struct NibbleConsts {
+    uint32_t m_lo, m_hi, e_lo, e_hi;
+};
+
+__device__ __forceinline__ NibbleConsts nibble_consts() {
+    NibbleConsts k{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+    asm volatile("" : "+v"(k.m_lo), "+v"(k.m_hi), "+v"(k.e_lo), "+v"(k.e_hi));
+    return k;
+}
+
+__device__ __forceinline__ float dot_chunk(const i32x4 w, const uint32_t (&xp)[16], const NibbleConsts &k) {
     float a[2] = {0.f, 0.f};   // two independent chains
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const uint32_t u = (uint32_t)w[t] ^ 0x88888888u;
         const uint32_t hi = u >> 8;
         float &c = a[t & 1];
-        c = dot2((u & 0x000F000Fu) | 0x64006400u, xp[4 * t + 0], c);
-        c = dot2((u & 0x00F000F0u) | 0x54005400u, xp[4 * t + 1], c);
-        c = dot2((hi & 0x000F000Fu) | 0x64006400u, xp[4 * t + 2], c);
-        c = dot2((hi & 0x00F000F0u) | 0x54005400u, xp[4 * t + 3], c);
+        c = dot2((u & k.m_lo) | k.e_lo, xp[4 * t + 0], c);
+        c = dot2((u & k.m_hi) | k.e_hi, xp[4 * t + 1], c);
+        c = dot2((hi & k.m_lo) | k.e_lo, xp[4 * t + 2], c);
+        c = dot2((hi & k.m_hi) | k.e_hi, xp[4 * t + 3], c);
     }
     return a[0] + a[1];
 }
@@ -278,7 +292,8 @@ __device__ __forceinline__ float row16_sum(float v) {
 template <int R, int KS, int MM>
 __global__ __launch_bounds__(256) void w4a16_gemv_kernel(W4A16Problem p, int lg) {
     constexpr int RG = 4 / KS;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kp = wave % KS, rg = wave / KS;
     const int n0 = (blockIdx.x * RG + rg) * R;
     const int m0 = blockIdx.y * MM;
@@ -307,20 +322,21 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(W4A16Problem p, int lg)
         for (int r = 0; r < R; ++r)
             acc[mm][r] = 0.f;
 
+    const NibbleConsts nk = nibble_consts();
     for (int c = c_begin + lane; c < c_end; c += 64) {
         i32x4 wv[R];
         uint16_t sv[R];
         i32x4 xv[MM][4];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            wv[r] = *reinterpret_cast<const i32x4 *>(wrow[r] + 16 * (int64_t)c);
-            sv[r] = srow[r][(32 * c) >> lg];
+            wv[r] = *reinterpret_cast<const i32x4 *>(wrow[r] + 16u * (uint32_t)c);
+            sv[r] = srow[r][(uint32_t)(32 * c) >> lg];
         }
 #pragma unroll
         for (int mm = 0; mm < MM; ++mm)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                xv[mm][t] = reinterpret_cast<const i32x4 *>(xrow[mm] + 32 * (int64_t)c)[t];
+                xv[mm][t] = reinterpret_cast<const i32x4 *>(xrow[mm] + 32u * (uint32_t)c)[t];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mm = 0; mm < MM; ++mm) {
@@ -330,7 +346,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(W4A16Problem p, int lg)
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const float s = (float)__builtin_bit_cast(_Float16, sv[r]);
-                acc[mm][r] += (dot_chunk(wv[r], xp) - off) * s;
+                acc[mm][r] += (dot_chunk(wv[r], xp, nk) - off) * s;
             }
         }
     }
