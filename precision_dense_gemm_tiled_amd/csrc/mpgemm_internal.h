@@ -131,6 +131,8 @@ enum W4A16Cfg {
     W4A16_RING4_128x64 = 13,   // ... 4-stage ring
     W4A16_SLICE_64x128_S4 = 14, // slice 64 x 128 over 4 stages of K (64 KiB LDS: two workgroups per CU)
     W4A16_SLICE_128x64_RING = 15, // slice 128 x 64 over 8 stages of K, activations through a 3-slot LDS ring
+    W4A16_GEMV_MFMA_NW4 = 16,  // decode on MFMA: 16 weight rows per workgroup, K over 4 wavefronts (G % 128 == 0)
+    W4A16_GEMV_MFMA_NW8 = 17,  // ... K over 8 wavefronts
     W4A16_CFG_COUNT
 };
 

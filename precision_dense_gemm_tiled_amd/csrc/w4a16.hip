@@ -378,6 +378,179 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(W4A16Problem p, int lg)
     }
 }
 
+// ---------------------------------------------------------------- MFMA GEMV path
+//
+// Decode shapes on the matrix unit. The VALU GEMV above spends most of its
+// instructions on the dot products; here v_mfma_f32_16x16x32_f16 takes them
+// and the VALU only dequantises, with the mask-or scheme of the GEMV (6
+// operations per 8 weights, pairs (k, k+4), values offset + u). A workgroup
+// owns 16 weight rows (the MFMA's columns) and all of K. Its MM activation
+// rows are the MFMA's rows 0 .. MM-1 (the other rows repeat the last one and
+// are never stored); they are staged once into LDS, already in the pair
+// order of the weights, and the staging pass also computes, per row and
+// 128-k step, the offset term c = sum over the step of 1032 x_k (k = 0..3
+// mod 8 in the low halves of the pairs of slots 0 and 2) and 72 x_k (slots 1
+// and 3). Each step's first MFMA starts from -c instead of 0, so the step ends
+// at sum x q exactly as in the GEMV, and one FMA applies the group scale (G a
+// multiple of 128: a step lies in one group).
+//
+// The NW wavefronts split K into contiguous step ranges. Lane (n, j) =
+// (lane % 16, lane / 16) loads the 16-byte run of 32 k at 32 j of each 128-k
+// step of weight row n; its word t (k = 32 j + 8 t ... + 7) is the B operand
+// of the step's MFMA t, and lane (m, j) reads the matching activations of row
+// m from LDS (all 16 lanes of a lane group read one address: a broadcast).
+// All weight loads of SPW steps are issued before the staging arithmetic.
+// The NW partial results meet in LDS and are added in wavefront order.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int NW, int MM, int SPW, int XPR>
+__global__ __launch_bounds__(NW * 64) void w4a16_gemv_mfma_kernel(W4A16Problem p, int lg) {
+    extern __shared__ __align__(16) uint8_t gm_smem[];
+    constexpr int NT = NW * 64;
+    const int K = p.K, S = K >> 7, CPR = K >> 3;   // 128-k steps, 16-byte chunks per row
+    uint16_t *xs = reinterpret_cast<uint16_t *>(gm_smem);                         // MM x K, pair order
+    float *negc = reinterpret_cast<float *>(gm_smem + (size_t)MM * K * 2);        // [S][MM]
+    float *red = negc + (size_t)S * MM;                                            // [NW][MM][16]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = blockIdx.x * 16, m0 = blockIdx.y * MM;
+    const int nl = lane & 15, j = lane >> 4;
+
+    // 1. this thread's activation chunks (chunk c = tid + u NT of each row)
+    i32x4 xr[MM][XPR];
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) {
+        const uint16_t *xrow = p.X + (int64_t)min(m0 + mm, p.M - 1) * p.ldx;
+#pragma unroll
+        for (int u = 0; u < XPR; ++u) {
+            // unconditional (clamped) loads keep the code straight, so the
+            // wait for them leaves the weight loads below in flight
+            const int c = min(tid + u * NT, CPR - 1);
+            xr[mm][u] = *reinterpret_cast<const i32x4 *>(xrow + 8 * c);
+        }
+    }
+
+    // 2. the weight runs and scales of the first SPW steps of this wavefront
+    const int spw = (S + NW - 1) / NW;
+    const int s_begin = min(S, wave * spw), s_end = min(S, s_begin + spw);
+    const int nrow = min(n0 + nl, p.N - 1);
+    const uint8_t *wrow = p.W + (int64_t)nrow * p.ldw_b + 16 * j;
+    const uint16_t *srow = p.S + (int64_t)nrow * p.lds;
+    i32x4 wv[SPW];
+    uint16_t sv[SPW];
+    auto issue = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            // a step past the range reloads the last one of the matrix (a
+            // wavefront with no steps at all loads it too, and uses nothing)
+            const int sg = c0 + i < s_end ? c0 + i : S - 1;
+            wv[i] = *reinterpret_cast<const i32x4 *>(wrow + 64u * (uint32_t)sg);
+            sv[i] = srow[(uint32_t)(128 * sg) >> lg];
+        }
+    };
+    issue(s_begin);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. pair the activations, store them, and the negated offset term of
+    //    every (row, step): the 16 chunks of a step sit in one 16-lane row
+    const uint32_t c1032 = 0x64086408u, c72 = 0x54805480u;
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm)
+#pragma unroll
+        for (int u = 0; u < XPR; ++u) {
+            const int c = tid + u * NT;
+            if (c < CPR) {   // uniform over each 16-lane row (CPR is a multiple of 16)
+                const i32x4 v = xr[mm][u];
+                const uint32_t d0 = (uint32_t)v[0], d1 = (uint32_t)v[1], d2 = (uint32_t)v[2], d3 = (uint32_t)v[3];
+                u32x4 pr;
+                pr[0] = __builtin_amdgcn_perm(d2, d0, 0x05040100u);   // k0, k4
+                pr[1] = __builtin_amdgcn_perm(d2, d0, 0x07060302u);   // k1, k5
+                pr[2] = __builtin_amdgcn_perm(d3, d1, 0x05040100u);   // k2, k6
+                pr[3] = __builtin_amdgcn_perm(d3, d1, 0x07060302u);   // k3, k7
+                float a0 = dot2(pr[0], c1032, 0.f), a1 = dot2(pr[1], c72, 0.f);
+                a0 = dot2(pr[2], c1032, a0);
+                a1 = dot2(pr[3], c72, a1);
+                const float t = row16_sum(a0 + a1);
+                *reinterpret_cast<u32x4 *>(xs + (size_t)mm * K + 8 * c) = pr;
+                if ((lane & 15) == 0)
+                    negc[(c >> 4) * MM + mm] = -t;
+            }
+        }
+    __syncthreads();
+
+    // 4. the steps: MFMA t of a step takes word t of every lane's run
+    const NibbleConsts nk = nibble_consts();
+    float y[MM];
+#pragma unroll
+    for (int r = 0; r < MM; ++r)
+        y[r] = 0.f;
+    const uint16_t *xa = xs + (size_t)min(nl, MM - 1) * K + 32 * j;
+    for (int c0 = s_begin; c0 < s_end; c0 += SPW) {
+        if (c0 != s_begin)
+            issue(c0);
+        // two steps at a time on independent accumulators (the 4 MFMAs of a
+        // step form one dependent chain); the second of an odd last pair
+        // repeats the first and is not added
+        static_assert(SPW % 2 == 0, "steps in pairs");
+#pragma unroll
+        for (int i = 0; i < SPW; i += 2) {
+            const int sg0 = c0 + i;
+            if (sg0 >= s_end)
+                break;
+            const bool has1 = sg0 + 1 < s_end;
+            const int sg[2] = {sg0, has1 ? sg0 + 1 : sg0};
+            f32x4 acc[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if constexpr (MM == 4) {
+                    acc[h] = *reinterpret_cast<const f32x4 *>(negc + 4 * sg[h]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[h][r] = negc[sg[h] * MM + min(r, MM - 1)];
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f16x8 a = *reinterpret_cast<const f16x8 *>(xa + 128 * sg[h] + 8 * t);
+                    const uint32_t u = (uint32_t)wv[i + h][t] ^ 0x88888888u;
+                    const uint32_t hi = u >> 8;
+                    u32x4 b;
+                    b[0] = (u & nk.m_lo) | nk.e_lo;
+                    b[1] = (u & nk.m_hi) | nk.e_hi;
+                    b[2] = (hi & nk.m_lo) | nk.e_lo;
+                    b[3] = (hi & nk.m_hi) | nk.e_hi;
+                    acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, b), acc[h], 0, 0, 0);
+                }
+            const float sc0 = (float)__builtin_bit_cast(_Float16, sv[i]);
+            const float sc1 = has1 ? (float)__builtin_bit_cast(_Float16, sv[i + 1]) : 0.f;
+#pragma unroll
+            for (int r = 0; r < MM; ++r)
+                y[r] = __builtin_fmaf(sc1, acc[1][r], __builtin_fmaf(sc0, acc[0][r], y[r]));
+        }
+    }
+
+    // 5. rows 0 .. MM-1 are registers 0 .. MM-1 of lanes 0-15; add the NW
+    //    wavefronts' results in order
+    if (j == 0) {
+#pragma unroll
+        for (int r = 0; r < MM; ++r)
+            red[(wave * MM + r) * 16 + nl] = y[r];
+    }
+    __syncthreads();
+    if (tid < MM * 16) {
+        const int r = tid >> 4, n = tid & 15;
+        float v = red[r * 16 + n];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            v += red[(w * MM + r) * 16 + n];
+        if (m0 + r < p.M && n0 + n < p.N)
+            p.Y[(int64_t)(m0 + r) * p.ldy + n0 + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
+    }
+}
+
 // ---------------------------------------------------------------- slice MFMA path
 //
 // Mid-size and prefill M. The weights dominate the bytes and the activations
@@ -1160,6 +1333,38 @@ static hipError_t launch_gemv(const W4A16Problem &p, hipStream_t stream, int lg)
     return launch_gemv_mm<R, KS, 4>(p, stream, lg);
 }
 
+// LDS of the MFMA GEMV: MM activation rows in pair order, the offset terms,
+// the wavefront partials.
+static constexpr int64_t GEMV_MFMA_LDS_MAX = 64 * 1024;
+static int64_t gemv_mfma_lds(int mm, int nw, int64_t K) {
+    return mm * K * 2 + (K / 128) * mm * 4 + (int64_t)nw * mm * 16 * 4;
+}
+
+template <int NW, int MM, int XPR>
+static hipError_t launch_gemv_mfma_mm(const W4A16Problem &p, hipStream_t stream, int lg) {
+    dim3 grid((p.N + 15) / 16, (p.M + MM - 1) / MM);
+    const size_t lds = (size_t)gemv_mfma_lds(MM, NW, p.K);
+    hipLaunchKernelGGL((w4a16_gemv_mfma_kernel<NW, MM, 8, XPR>), grid, dim3(NW * 64), lds, stream, p, lg);
+    return hipGetLastError();
+}
+
+// G a multiple of 128, the activation rows of a workgroup within 64 KiB of
+// LDS and within what the threads stage in one pass (K <= 2048 XPR NW / 4);
+// other shapes run the VALU GEMV.
+template <int NW>
+static hipError_t launch_gemv_mfma(const W4A16Problem &p, hipStream_t stream, int lg) {
+    const int mm = p.M == 1 ? 1 : p.M == 2 ? 2 : 4;
+    const int64_t chunks = p.K / 8;
+    if (lg < 7 || gemv_mfma_lds(mm, NW, p.K) > GEMV_MFMA_LDS_MAX || chunks > 4 * NW * 64)
+        return p.M == 1 ? launch_gemv<2, 2>(p, stream, lg) : launch_gemv<4, 2>(p, stream, lg);
+    const bool x2 = chunks <= 2 * NW * 64;
+    if (mm == 1)
+        return x2 ? launch_gemv_mfma_mm<NW, 1, 2>(p, stream, lg) : launch_gemv_mfma_mm<NW, 1, 4>(p, stream, lg);
+    if (mm == 2)
+        return x2 ? launch_gemv_mfma_mm<NW, 2, 2>(p, stream, lg) : launch_gemv_mfma_mm<NW, 2, 4>(p, stream, lg);
+    return x2 ? launch_gemv_mfma_mm<NW, 4, 2>(p, stream, lg) : launch_gemv_mfma_mm<NW, 4, 4>(p, stream, lg);
+}
+
 template <int MB, int NB, int WN, int WK, int NST, int PD, int RG>
 static hipError_t launch_slice(const W4A16Problem &p, const W4A16Plan &plan, const W4A16Workspace &ws,
                                hipStream_t stream, int lg) {
@@ -1304,7 +1509,9 @@ const char *w4a16_cfg_name(int cfg) {
         "slice 16 x 16, K over 4 wavefronts", "slice 32 x 32, K over 2 wavefronts",
         "slice 64 x 128", "slice 128 x 128", "ring 128 x 64, 3 stages", "ring 128 x 64, 4 stages",
         "slice 64 x 128, 4 stages (two workgroups per compute unit)",
-        "slice 128 x 64, 8 stages through a 3-slot activation ring"};
+        "slice 128 x 64, 8 stages through a 3-slot activation ring",
+        "mfma gemv, 16 rows per workgroup, K over 4 wavefronts",
+        "mfma gemv, 16 rows per workgroup, K over 8 wavefronts"};
     return cfg >= 0 && cfg < W4A16_CFG_COUNT ? names[cfg] : "?";
 }
 
@@ -1315,10 +1522,15 @@ int choose_w4a16_cfg(int64_t M, int64_t N, int64_t K) {
     // 128 rows the 64 x 128 slices win (M = 80: 12.6 vs 14.9 us for the ring
     // kernel, M = 128: 12.7 vs 15.0), above 128 the ring kernel (M = 160: 19.5
     // vs 20.4 us, 256: 20.0 vs 22.7; 512: 27.4 vs 45.0)
+    // M = 1: the VALU GEMV (4.22 us against 4.49 for the matrix-unit GEMV,
+    // whose one wavefront per SIMD with 8 weight loads each waits longer on
+    // the cold weights than the GEMV's four with 2 each); 2 ... 4 rows: the
+    // matrix-unit GEMV, whose arithmetic does not grow with M (M = 2: 4.56
+    // vs 5.16 us, M = 4: 4.81 vs 6.70; VALU GEMV for G < 128)
     if (M == 1)
         return W4A16_GEMV_R2_KS2;
     if (M <= 4)
-        return W4A16_GEMV_R4_KS2;
+        return W4A16_GEMV_MFMA_NW4;
     if (M <= 16)
         return W4A16_SLICE_16x16_K4;
     if (M <= 32)
@@ -1343,6 +1555,8 @@ static hipError_t launch_one(const W4A16Problem &p, const W4A16Plan &plan, const
     case W4A16_GEMV_R2_KS1: return launch_gemv<2, 1>(p, stream, lg);
     case W4A16_GEMV_R4_KS1: return launch_gemv<4, 1>(p, stream, lg);
     case W4A16_GEMV_R8_KS1: return launch_gemv<8, 1>(p, stream, lg);
+    case W4A16_GEMV_MFMA_NW4: return launch_gemv_mfma<4>(p, stream, lg);
+    case W4A16_GEMV_MFMA_NW8: return launch_gemv_mfma<8>(p, stream, lg);
 #define MPG_LAUNCH(C, mb, nb, wn, wk, nst, pd, rg) \
     case C: return launch_slice<mb, nb, wn, wk, nst, pd, rg>(p, plan, ws, stream, lg);
         MPG_SLICE_CONFIGS(MPG_LAUNCH)

@@ -371,7 +371,7 @@ def _check_w4(X, W, S, K, G, what):
     assert bad.size == 0, f"{what}: {len(bad)} outside the bar, worst {err.max()}"
 
 
-@pytest.mark.parametrize("M", [1, 16, 128])
+@pytest.mark.parametrize("M", [1, 4, 16, 128])
 def test_w4a16_config4(M):
     N = K = 4096
     G = 128
@@ -387,7 +387,7 @@ def test_w4a16_ragged(M, N, K, G):
     _check_w4(X, W, S, K, G, f"w4a16 {M}x{N}x{K} G={G}")
 
 
-W4A16_CFGS = 16
+W4A16_CFGS = 18
 
 
 @pytest.mark.parametrize("M,N,K,G", [(96, 4096, 4096, 128), (256, 4096, 4096, 128), (512, 4096, 4096, 128),
@@ -405,10 +405,10 @@ def test_w4a16_prefill_sizes(M, N, K, G):
 def test_w4a16_every_config(monkeypatch):
     """Each weight-only kernel configuration (forced through the ablation
     override) on ragged shapes, group sizes 32 ... 256 and the decode layer,
-    plus the bit-exact small-integer case."""
+    plus the bit-exact small-integer cases (G = 64 and 128)."""
     shapes = [(1, 4096, 4096, 128), (1, 50, 96, 32), (2, 70, 512, 64), (3, 33, 256, 128),
               (5, 130, 1024, 256), (17, 40, 4096, 4096), (16, 4096, 4096, 128), (128, 1000, 4096, 128),
-              (40, 200, 1440, 32), (130, 70, 640, 128)]
+              (40, 200, 1440, 32), (130, 70, 640, 128), (2, 100, 6144, 128), (3, 64, 8192, 256)]
     problems = [(shape, inputs.w4a16_problem(*shape, seed=sum(shape) + 7)) for shape in shapes]
     refs = [oracle.gemm_w4a16(X, W, S, shape[2], shape[3], want_t2=True) for shape, (X, W, S) in problems]
     r = np.random.default_rng(5)
@@ -416,6 +416,9 @@ def test_w4a16_every_config(monkeypatch):
     Wi = r.integers(0, 256, (96, 1024)).astype(np.uint8)
     Si = (2.0 ** -r.integers(3, 9, (96, 2048 // 64))).astype(np.float16)
     yi = oracle.f16_encode_rne_array(oracle.gemm_w4a16(Xi, Wi, Si, 2048, 64))
+    # the same with G = 128 (the group size the matrix-unit GEMV needs)
+    Si2 = (2.0 ** -r.integers(3, 9, (96, 2048 // 128))).astype(np.float16)
+    yi2 = oracle.f16_encode_rne_array(oracle.gemm_w4a16(Xi, Wi, Si2, 2048, 128))
     for cfg in range(W4A16_CFGS):
         monkeypatch.setenv("MPGEMM_W4A16_CFG", str(cfg))
         with mp.Handle() as h:
@@ -433,6 +436,8 @@ def test_w4a16_every_config(monkeypatch):
             # twice in a row: the split-K arrival counters must be back at zero
             got = host(mp.gemm_w4a16(dev(Xi), dev(Wi), dev(Si), 64, handle=h.value)).view(np.uint16)
             assert np.array_equal(got, yi), f"cfg {cfg}: second call differs"
+            got = host(mp.gemm_w4a16(dev(Xi), dev(Wi), dev(Si2), 128, handle=h.value)).view(np.uint16)
+            assert np.array_equal(got, yi2), f"cfg {cfg}: small-integer case (G = 128) not bit-exact"
             z = mp.gemm_w4a16(dev(np.zeros((3, 0), np.float16)), dev(np.zeros((5, 0), np.uint8)),
                               dev(np.zeros((5, 0), np.float16)), 32, handle=h.value)
             assert np.array_equal(host(z).astype(np.float64), np.zeros((3, 5))), f"cfg {cfg}: K = 0"
@@ -454,7 +459,7 @@ def test_w4a16_one_hot_exact(G):
         assert np.array_equal(got[i], oracle.f16_encode_rne_array(exact)), f"k={k}"
 
 
-@pytest.mark.parametrize("M,G", [(1, 128), (16, 128), (128, 128), (16, 64)])
+@pytest.mark.parametrize("M,G", [(1, 128), (2, 128), (4, 256), (16, 128), (128, 128), (16, 64)])
 def test_w4a16_exact_small_integers(M, G):
     """Small-integer x and power-of-two scales: every partial sum is exact in
     fp32, so Y must be the fp16 rounding of the exact sum, bit for bit."""
@@ -468,13 +473,13 @@ def test_w4a16_exact_small_integers(M, G):
 
 
 @pytest.mark.parametrize("M,N,K,G,cfg", [(9, 40, 256, 128, None), (200, 100, 1440, 32, 12), (150, 70, 512, 64, 12),
-                                         (40, 72, 640, 128, 10)])
+                                         (40, 72, 640, 128, 10), (3, 50, 1152, 128, None), (1, 50, 1152, 128, None)])
 def test_w4a16_strided(M, N, K, G, cfg, monkeypatch):
     """Operands with padded rows (NaN activations and scales, 0x88 weights
     past K) and an output with padded columns: nothing past K or N is read
-    into a result or written; for the default small-M kernel, the ring
-    kernel (ragged M, N and a partial last stage, K split over workgroups)
-    and the slice kernel."""
+    into a result or written; for the default kernels at M = 9 (slice), 3
+    (matrix-unit GEMV) and 1 (VALU GEMV), the ring kernel (ragged M, N and a
+    partial last stage, K split over workgroups) and the slice kernel."""
     import torch
     if cfg is not None:
         monkeypatch.setenv("MPGEMM_W4A16_CFG", str(cfg))

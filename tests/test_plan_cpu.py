@@ -158,14 +158,14 @@ def test_plan_gemm_arguments(mp):
 
 
 def test_w4a16_plan_at_the_workload_sizes(mp):
-    """N = K = 4096: GEMV for M = 1 (2 rows per wavefront) and M <= 4 (4 rows),
-    16 x 16 slices with K inside the workgroup at M = 16, 32 x 32 slices with K
+    """N = K = 4096: the VALU GEMV for M = 1 (2 rows per wavefront), the
+    matrix-unit GEMV for M = 2 ... 4 (16 rows per workgroup), 16 x 16 slices with K inside the workgroup at M = 16, 32 x 32 slices with K
     split in 2 at M = 32, 64 x 128 slices over 4 stages with K split in 8 at
     M = 33 ... 64, 64 x 128 slices with K split in 4 at M = 65 ... 128;
     above 128 rows, the 128 x 64 ring kernel, K split until the grid covers
     the 256 compute units (M = 256: 128 tiles, 2 slices; M >= 512: no
     split)."""
-    want = {1: (3, 1), 2: (4, 1), 4: (4, 1), 16: (8, 1), 32: (9, 2), 33: (14, 8), 64: (14, 8), 65: (10, 4),
+    want = {1: (3, 1), 2: (16, 1), 4: (16, 1), 16: (8, 1), 32: (9, 2), 33: (14, 8), 64: (14, 8), 65: (10, 4),
             96: (10, 4),
             127: (10, 4), 128: (10, 4), 129: (12, 2), 192: (12, 2), 256: (12, 2), 512: (12, 1), 1024: (12, 1),
             4096: (12, 1)}
