@@ -133,6 +133,8 @@ enum W4A16Cfg {
     W4A16_SLICE_128x64_RING = 15, // slice 128 x 64 over 8 stages of K, activations through a 3-slot LDS ring
     W4A16_GEMV_MFMA_NW4 = 16,  // decode on MFMA: 16 weight rows per workgroup, K over 4 wavefronts (G % 128 == 0)
     W4A16_GEMV_MFMA_NW8 = 17,  // ... K over 8 wavefronts
+    W4A16_PC_64x128 = 18,      // slice 64 x 128: 4 producer + 4 consumer wavefronts around a 4-slot LDS ring
+    W4A16_PC_64x128_C8 = 19,   // ... 4 producer + 8 consumer wavefronts (64 x 16 each)
     W4A16_CFG_COUNT
 };
 

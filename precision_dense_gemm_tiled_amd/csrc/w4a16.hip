@@ -575,20 +575,32 @@ __global__ __launch_bounds__(NW * 64) void w4a16_gemv_mfma_kernel(W4A16Problem p
 // workspace and a second kernel adds the slices in slice order.
 
 // 8 packed nibbles (k = 0..7, low nibble first) -> 8 fp16 values q * s in
-// natural k order, 18 VALU operations: the even-k nibbles stay at bits 0-3 of
-// each byte, the odd-k ones at bits 4-7; one byte permute per pair builds
-// (nibble, 0, nibble << 4, 0), and one XOR flips the sign bit of both (u =
-// nibble ^ 8 = q + 8) and sets the exponents that make the halves read
-// 1024 + u and 64 + u'; subtracting (1032, 72) leaves q exactly.
-__device__ __forceinline__ f16x8 dequant8_perm(uint32_t w, f16x2 s2) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = w & 0xF0F0F0F0u;
+// natural k order, 16 VALU operations: per byte b, one byte permute of the
+// word and a constant builds (byte, 0x64, byte, 0x54), one three-input bit
+// operation keeps the even-k nibble in bits 0-3 and the odd-k one in bits
+// 4-7 of the two bytes while flipping their top bits (u = nibble ^ 8 = q + 8),
+// so the halves read 1024 + u and 64 + u'; subtracting (1032, 72) leaves q
+// exactly, and one multiply applies the scale. The three constants sit in
+// VGPRs (gfx9's three-operand encoding takes no literal).
+struct PermConsts {
+    uint32_t expo, mask, flip;
+};
+
+__device__ __forceinline__ PermConsts perm_consts() {
+    PermConsts k{0x00005464u, 0xFFF0FF0Fu, 0x00800008u};
+    asm volatile("" : "+v"(k.expo), "+v"(k.mask), "+v"(k.flip));
+    return k;
+}
+
+__device__ __forceinline__ f16x8 dequant8_perm(uint32_t w, f16x2 s2, const PermConsts &k) {
     const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-72.0f};
     f16x2 q[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        // result bytes: lo.b, 0, hi.b, 0 (v_perm: src1 = bytes 0-3, src0 = 4-7, selector 12 = zero)
-        const uint32_t sel = (uint32_t)b | (12u << 8) | ((4u + b) << 16) | (12u << 24);
-        const uint32_t pr = __builtin_amdgcn_perm(hi, lo, sel) ^ 0x54806408u;
+        // result bytes: w.b, expo.0, w.b, expo.1 (v_perm: selector 0-3 pick the
+        // second source's bytes, 4-7 the first's)
+        const uint32_t sel = (uint32_t)b | (4u << 8) | ((uint32_t)b << 16) | (5u << 24);
+        const uint32_t pr = (__builtin_amdgcn_perm(k.expo, w, sel) & k.mask) ^ k.flip;
         q[b] = (__builtin_bit_cast(f16x2, pr) + bias) * s2;
     }
     return f16x8{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
@@ -606,7 +618,9 @@ __device__ __forceinline__ int xcd_contiguous(int id, int nblk) {
 }
 
 
-template <int MB, int NB, int WN, int WK, int NST, int PDT, int RG>
+// KF: K is a multiple of 128 (so are the K slices), every step that starts
+// inside the range lies wholly inside it, and the load clamps are scalar.
+template <int MB, int NB, int WN, int WK, int NST, int PDT, int RG, bool KF>
 __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16Split sk, int lg) {
     static_assert(WN * WK == 4, "4 wavefronts");
     constexpr int BM = 16 * MB, BN = 16 * NB * WN;
@@ -685,14 +699,23 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
             const int u = wave + 4 * v;                 // unit of this step: (block group, half, rows)
             const int b = (u / (4 * MB)) * NST + s;     // block
             const int h = (u / (2 * MB)) % 2, q = u % (2 * MB);   // half, 8-row group
-            const int k = min(k_begin + 128 * b + 64 * h + xc8[v], p.K - 8);
+            int k;
+            if constexpr (KF)
+                k = min(k_begin + 128 * b, p.K - 128) + 64 * h + xc8[v];   // scalar clamp
+            else
+                k = min(k_begin + 128 * b + 64 * h + xc8[v], p.K - 8);
             dma16(xrow[v] + k, xs + (RG > 0 ? b % RG : b) * BLOCK + h * PB + q * 1024);
         }
         asm volatile("" ::: "memory");
     };
     auto issue_w = [&](int s) {
-        int k = kw + 128 * s + 32 * pig;
-        k = k + 32 <= p.K ? k : p.K - 32;
+        int k;
+        if constexpr (KF) {
+            k = min(kw + 128 * s, p.K - 128) + 32 * pig;   // scalar clamp
+        } else {
+            k = kw + 128 * s + 32 * pig;
+            k = k + 32 <= p.K ? k : p.K - 32;
+        }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             wr[s][j] = *reinterpret_cast<const i32x4 *>(wrow[j] + (k >> 1));
@@ -724,6 +747,7 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
 #pragma unroll
         for (int j = 0; j < NB; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const PermConsts pk = perm_consts();
     // per-lane part of the fragment address of MFMA step t: quarter pi(g)
     // (half pi(g) / 2, chunks 4 (pi(g) % 2) + t), row 16 i + l % 16 (16 i
     // does not change the swizzle bits)
@@ -748,25 +772,37 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
         }
         if (kw + 128 * s >= k_end)
             continue;   // (the barriers above stay uniform across the wavefronts)
-        const bool live = kw + 128 * s + 32 * pig < k_end;
+        const bool live = KF || kw + 128 * s + 32 * pig < k_end;
         const uint8_t *blk = xs + (RG > 0 ? (wk * NST + s) % RG : wk * NST + s) * BLOCK;
+        // every fragment of the step in its own registers: all LDS reads go
+        // out at once and the dequantisation runs in their shadow, then the
+        // MFMAs follow back to back (with one set of fragment registers
+        // reused per k-step, each k-step waited on its reads and on the
+        // previous MFMAs' operand reads before its dequantisation)
+        f16x8 a[4][MB];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            f16x8 a[MB];
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < MB; ++i)
-                a[i] = *reinterpret_cast<const f16x8 *>(blk + aoff[t] + i * 2048);
+                a[t][i] = *reinterpret_cast<const f16x8 *>(blk + aoff[t] + i * 2048);
+        f16x8 b[4][NB];
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
+        for (int j = 0; j < NB; ++j) {
+            const _Float16 sc = __builtin_bit_cast(_Float16, sr[s][j]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
                 // a run past the K range gets q = 0 (u = 8 in every nibble)
                 const uint32_t w = live ? (uint32_t)wr[s][j][t] : 0u;
-                const _Float16 sc = __builtin_bit_cast(_Float16, sr[s][j]);
-                const f16x8 b = dequant8_perm(w, f16x2{sc, sc});
-#pragma unroll
-                for (int i = 0; i < MB; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b, acc[i][j], 0, 0, 0);
+                b[t][j] = dequant8_perm(w, f16x2{sc, sc}, pk);
             }
         }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t][i], b[t][j], acc[i][j], 0, 0, 0);
     }
 
     // 4. add the WK partial sums through LDS (reusing the activation buffer)
@@ -808,6 +844,179 @@ __global__ __launch_bounds__(256) void w4a16_slice_kernel(W4A16Problem p, W4A16S
         return;
     }
     // only the wavefronts with wk == 0 get here; they are the first WN
+    float *mine = sk.partial + (int64_t)logical * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                mine[((i * NB + j) * 4 + r) * (64 * WN) + tid] = acc[i][j][r];
+}
+
+// ---------------------------------------------------------------- producer/consumer slices
+//
+// The slice kernel's wavefronts both issue their loads and run the products,
+// and a load that the memory system cannot take yet holds up the wavefront's
+// instruction stream, MFMAs included: with the weights cold, a wavefront of
+// the 64 x 128 slices spends about a third of its time in load issue (clock
+// stamps per wavefront). Here the roles are split: the last 4 wavefronts
+// only move the activations and the weights of each 128-k step into an
+// R-slot LDS ring with direct-to-LDS loads, keeping up to R - 1 steps in
+// flight, and the first NC only read LDS, dequantise and run the MFMAs (the
+// tile and partial layout of the slice kernel with NC column wavefronts, so
+// its K-slice sum kernel applies). One barrier per step: before barrier s the
+// producers have waited for step s's loads and the consumers have finished
+// step s - 1, whose slot the producers refill with step s + R - 1 after it.
+//
+// Slot layout: the activation block of the slice kernel (two 64-k halves of
+// BM rows x 128 bytes, chunk c of row r at c ^ ((r / 2) & 7)), then the
+// weights, tile row n's 64 bytes at 64 n with its 16-byte quarter q at slot
+// q ^ ((n / 4) & 3) (one direct-to-LDS load moves 16 whole rows; the slots
+// make the 16 rows a consumer lane group reads hit 16 bank groups). The
+// group scales of the workgroup's whole K range sit in a table filled by the
+// consumers before the first barrier. K must be a multiple of 128.
+template <int MB, int NB, int NC, int R, int NSTMAX>
+__global__ __launch_bounds__((NC + 4) * 64) void w4a16_pc_kernel(W4A16Problem p, W4A16Split sk, int lg) {
+    constexpr int WN = NC, BM = 16 * MB, BN = 16 * NB * WN, CT = NC * 64;
+    constexpr int PB = BM * 128, XBLK = 2 * PB, WBLK = BN * 64, SLOT = XBLK + WBLK;
+    constexpr int XUP = XBLK / 1024 / 4, WUP = WBLK / 1024 / 4;   // loads per producer per step
+    static_assert(XUP == MB && WUP * 4 * 16 == BN, "units");
+    __shared__ __attribute__((aligned(16))) uint8_t ring[R * SLOT];
+    __shared__ uint16_t stab[NSTMAX * 4 * BN];   // [step][quarter][column]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int logical = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int ks = logical % sk.ks;
+    const int tile = logical / sk.ks;
+    const int mb = tile % sk.mblocks, ng = tile / sk.mblocks;
+    const int m0 = mb * BM, n0 = ng * BN;
+    const int k_begin = ks * sk.kslice;
+    const int k_end = min(p.K, k_begin + sk.kslice);
+    const int NS = (k_end - k_begin) >> 7;   // steps of this workgroup (K % 128 == 0)
+
+    if (wave >= NC) {
+        // ------------------------------------------------ producers
+        const int pw = wave - NC;
+        // activation unit u = pw + 4 v (half u / (2 MB), 8-row group u % (2 MB));
+        // lane l: row 8 q + l / 8, chunk (l % 8) ^ ((row / 2) % 8)
+        const uint16_t *xsrc[XUP];
+        int xdst[XUP];
+#pragma unroll
+        for (int v = 0; v < XUP; ++v) {
+            const int u = pw + 4 * v;
+            const int h = u / (2 * MB), q = u % (2 * MB);
+            const int r = 8 * q + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            xsrc[v] = p.X + (int64_t)min(m0 + r, p.M - 1) * p.ldx + k_begin + 64 * h + 8 * c;
+            xdst[v] = h * PB + q * 1024;
+        }
+        // weight unit wu = pw + 4 v: tile rows 16 wu ... + 15, lane l: row
+        // 16 wu + l / 4, slot l % 4 holding quarter (l % 4) ^ ((row / 4) & 3)
+        const uint8_t *wsrc[WUP];
+#pragma unroll
+        for (int v = 0; v < WUP; ++v) {
+            const int wu = pw + 4 * v;
+            const int row = 16 * wu + (lane >> 2);
+            const int q = (lane & 3) ^ ((row >> 2) & 3);
+            wsrc[v] = p.W + (int64_t)min(n0 + row, p.N - 1) * p.ldw_b + (k_begin >> 1) + 16 * q;
+        }
+        auto issue = [&](int s) {
+            uint8_t *slot = ring + (s % R) * SLOT;
+#pragma unroll
+            for (int v = 0; v < XUP; ++v)
+                dma16(xsrc[v] + 128 * s, slot + xdst[v]);
+#pragma unroll
+            for (int v = 0; v < WUP; ++v)
+                dma16(wsrc[v] + 64 * s, slot + XBLK + (pw + 4 * v) * 1024);
+            asm volatile("" ::: "memory");
+        };
+        for (int s = 0; s < R - 1 && s < NS; ++s)
+            issue(s);
+        for (int s = 0; s < NS; ++s) {
+            // outstanding: steps s ... min(s + R - 2, NS - 1); step s must have landed
+            const int younger = min(R - 2, NS - 1 - s);
+            wait_vm_lds_n(younger * (XUP + WUP));
+            lds_barrier();
+            if (s + R - 1 < NS)
+                issue(s + R - 1);
+        }
+        return;
+    }
+
+    // ---------------------------------------------------- consumers
+    const int wn = wave, g = lane >> 4;
+    const int pig = ((g & 1) << 1) | (g >> 1);   // this lane group's 32-k quarter
+    const int n0w = n0 + wn * 16 * NB;
+    // the scale table: entry (s, q, col) = S[n0 + col][(k_begin + 128 s + 32 q) >> lg]
+    for (int e = tid; e < NS * 4 * BN; e += CT) {
+        const int col = e % BN, q = (e / BN) % 4, st = e / (4 * BN);
+        const int n = min(n0 + col, p.N - 1);
+        stab[e] = p.S[(int64_t)n * p.lds + ((k_begin + 128 * st + 32 * q) >> lg)];
+    }
+    int aoff[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int r = lane & 15;
+        aoff[t] = (pig >> 1) * PB + r * 128 + (((4 * (pig & 1) + t) ^ ((r >> 1) & 7)) * 16);
+    }
+    int woff[NB], soff[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int row = wn * 16 * NB + 16 * j + (lane & 15);
+        woff[j] = XBLK + row * 64 + ((pig ^ ((row >> 2) & 3)) * 16);
+        soff[j] = pig * BN + row;
+    }
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const PermConsts pk = perm_consts();
+    for (int s = 0; s < NS; ++s) {
+        wait_lds_only();   // the scale table (s = 0) and this wavefront's reads of step s - 1
+        lds_barrier();
+        const uint8_t *slot = ring + (s % R) * SLOT;
+        i32x4 wv[NB];
+        _Float16 sc[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            wv[j] = *reinterpret_cast<const i32x4 *>(slot + woff[j]);
+            sc[j] = __builtin_bit_cast(_Float16, stab[s * 4 * BN + soff[j]]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f16x8 a[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                a[i] = *reinterpret_cast<const f16x8 *>(slot + aoff[t] + i * 2048);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const f16x8 b = dequant8_perm((uint32_t)wv[j][t], f16x2{sc[j], sc[j]}, pk);
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b, acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+
+    // store Y directly, or this K slice's partial tile in the slice kernel's
+    // register order (consumer thread tid = 64 wn + lane)
+    if (sk.ks == 1) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + 16 * i + 4 * g + r, n = n0w + 16 * j + (lane & 15);
+                    if (m < p.M && n < p.N)
+                        p.Y[(int64_t)m * p.ldy + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
+                }
+        return;
+    }
     float *mine = sk.partial + (int64_t)logical * (BM * BN);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -1111,6 +1320,7 @@ __global__ __launch_bounds__(256) void w4a16_ring_kernel(W4A16Problem p, W4A16Sp
         }
         return R;
     };
+    const PermConsts pk = perm_consts();
     auto dequant = [&](const RingRaw &R, RingFrag &F) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -1119,7 +1329,7 @@ __global__ __launch_bounds__(256) void w4a16_ring_kernel(W4A16Problem p, W4A16Sp
                 F.a[t][i] = R.a[t][i];
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                F.b[t][j] = dequant8_perm(R.wq[j][t], R.sc[j]);
+                F.b[t][j] = dequant8_perm(R.wq[j][t], R.sc[j], pk);
         }
     };
     auto mfma = [&](const RingFrag &F) {
@@ -1174,7 +1384,7 @@ __global__ __launch_bounds__(256) void w4a16_ring_kernel(W4A16Problem p, W4A16Sp
                 __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.a[t][i0 + 1], cur.b[t][j], acc[i0 + 1][j], 0, 0, 0);
             if (g >= 4) {
                 const int tt = (g - 4) / 2, jj = (g - 4) % 2;
-                nxt.b[tt][jj] = dequant8_perm(R.wq[jj][tt], R.sc[jj]);
+                nxt.b[tt][jj] = dequant8_perm(R.wq[jj][tt], R.sc[jj], pk);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1379,13 +1589,45 @@ static hipError_t launch_slice(const W4A16Problem &p, const W4A16Plan &plan, con
     const int64_t blocks = tiles * sk.ks;
     if (blocks > INT_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((w4a16_slice_kernel<MB, NB, WN, WK, NST, PD, RG>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       p, sk, lg);
+    if (p.K % 128 == 0)
+        hipLaunchKernelGGL((w4a16_slice_kernel<MB, NB, WN, WK, NST, PD, RG, true>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, p, sk, lg);
+    else
+        hipLaunchKernelGGL((w4a16_slice_kernel<MB, NB, WN, WK, NST, PD, RG, false>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, p, sk, lg);
     if (sk.ks == 1)
         return hipGetLastError();
     const int64_t total = tiles * BM * BN / 4;   // one thread per 4 outputs
     hipLaunchKernelGGL((w4a16_reduce_kernel<MB, NB, WN>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                        stream, p, sk);
+    return hipGetLastError();
+}
+
+// K % 128 != 0 runs the equivalent slice kernel (64 x 128, 8 steps).
+template <int MB, int NB, int NC, int R, int NSTMAX>
+static hipError_t launch_pc(const W4A16Problem &p, const W4A16Plan &plan, const W4A16Workspace &ws,
+                            hipStream_t stream, int lg) {
+    if (p.K % 128 != 0 || plan.kslice > 128 * NSTMAX)
+        return launch_slice<MB, 2, 4, 1, NSTMAX, 2, 0>(p, plan, ws, stream, lg);
+    static_assert(NB * NC == 8, "the fallback's 64 x 128 tile");
+    constexpr int BM = 16 * MB, BN = 16 * NB * NC;
+    W4A16Split sk;
+    sk.mblocks = plan.mblocks;
+    sk.ngroups = plan.ngroups;
+    sk.ks = plan.ks;
+    sk.kslice = plan.kslice;
+    sk.partial = ws.partial;
+    const int64_t tiles = (int64_t)sk.mblocks * sk.ngroups;
+    const int64_t blocks = tiles * sk.ks;
+    if (blocks > INT_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((w4a16_pc_kernel<MB, NB, NC, R, NSTMAX>), dim3((unsigned)blocks), dim3((NC + 4) * 64), 0,
+                       stream, p, sk, lg);
+    if (sk.ks == 1)
+        return hipGetLastError();
+    const int64_t total = tiles * BM * BN / 4;
+    hipLaunchKernelGGL((w4a16_reduce_kernel<MB, NB, NC>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       p, sk);
     return hipGetLastError();
 }
 
@@ -1429,6 +1671,11 @@ static hipError_t launch_ring(const W4A16Problem &p, const W4A16Plan &plan, cons
     X(W4A16_SLICE_64x128_S4, 4, 2, 4, 1, 4, 2, 0)  \
     X(W4A16_SLICE_128x64_RING, 8, 1, 4, 1, 8, 2, 3)
 
+// The producer/consumer slices, in the same shape notation (pd = ring slots).
+#define MPG_PC_CONFIGS(X)                 \
+    X(W4A16_PC_64x128, 4, 2, 4, 1, 8, 4, 0) \
+    X(W4A16_PC_64x128_C8, 4, 1, 8, 1, 8, 4, 0)
+
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cfg, int cu_count, int64_t partial_floats) {
     W4A16Plan plan{K == 0 ? (int)W4A16_GEMV_R2_KS2 : cfg, 1, 0, 0, 0};
     int MB = 0, NB = 0, WN = 0, WK = 0, NST = 0;
@@ -1436,6 +1683,7 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int cfg, int cu_count, int
 #define MPG_SHAPE(C, mb, nb, wn, wk, nst, pd, rg) \
     case C: MB = mb; NB = nb; WN = wn; WK = wk; NST = nst; break;
         MPG_SLICE_CONFIGS(MPG_SHAPE)
+        MPG_PC_CONFIGS(MPG_SHAPE)
 #undef MPG_SHAPE
     case W4A16_RING3_128x64:
     case W4A16_RING4_128x64: {
@@ -1494,6 +1742,7 @@ int64_t w4a16_plan_scratch_floats(const W4A16Plan &plan) {
 #define MPG_SCRATCH(C, mb, nb, wn, wk, nst, pd, rg) \
     case C: return (int64_t)plan.ks * plan.mblocks * plan.ngroups * (16 * mb) * (16 * nb * wn);
         MPG_SLICE_CONFIGS(MPG_SCRATCH)
+        MPG_PC_CONFIGS(MPG_SCRATCH)
 #undef MPG_SCRATCH
     case W4A16_RING3_128x64:
     case W4A16_RING4_128x64:
@@ -1511,7 +1760,9 @@ const char *w4a16_cfg_name(int cfg) {
         "slice 64 x 128, 4 stages (two workgroups per compute unit)",
         "slice 128 x 64, 8 stages through a 3-slot activation ring",
         "mfma gemv, 16 rows per workgroup, K over 4 wavefronts",
-        "mfma gemv, 16 rows per workgroup, K over 8 wavefronts"};
+        "mfma gemv, 16 rows per workgroup, K over 8 wavefronts",
+        "slice 64 x 128, 4 producer + 4 consumer wavefronts, 4-slot LDS ring",
+        "slice 64 x 128, 4 producer + 8 consumer wavefronts, 4-slot LDS ring"};
     return cfg >= 0 && cfg < W4A16_CFG_COUNT ? names[cfg] : "?";
 }
 
@@ -1561,6 +1812,10 @@ static hipError_t launch_one(const W4A16Problem &p, const W4A16Plan &plan, const
     case C: return launch_slice<mb, nb, wn, wk, nst, pd, rg>(p, plan, ws, stream, lg);
         MPG_SLICE_CONFIGS(MPG_LAUNCH)
 #undef MPG_LAUNCH
+#define MPG_LAUNCH_PC(C, mb, nb, wn, wk, nst, pd, rg) \
+    case C: return launch_pc<mb, nb, wn, pd, nst>(p, plan, ws, stream, lg);
+        MPG_PC_CONFIGS(MPG_LAUNCH_PC)
+#undef MPG_LAUNCH_PC
     case W4A16_RING3_128x64: return launch_ring<3>(p, plan, ws, stream, lg);
     case W4A16_RING4_128x64: return launch_ring<4>(p, plan, ws, stream, lg);
     default: return hipErrorInvalidValue;
