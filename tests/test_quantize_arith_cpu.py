@@ -5,17 +5,20 @@ s = fp16(max|w| / 7), q = clamp(round_half_even(w / s), -8, 7), the reading
 of the "fused-int4-gemm-sm75" README's per-group scales) avoids exact
 arithmetic in two places:
 
-1. the scale is fp16(fp32(amax) / 7.0f): an fp32 quotient rounded again to
-   fp16, claimed equal to rounding the exact quotient amax / 7 once;
-2. the code is rint(w * (1/s)) in fp32 (the reciprocal correctly rounded, or
-   one ulp off), corrected only where the fp32 remainder w - q s is exactly
-   +-s/2 (a tie) and q is odd; claimed equal to round_half_even(w / s).
+1. the scale is fp16(fp32(amax) * fp32(1/7)): an fp32 product rounded again
+   to fp16, claimed equal to rounding the exact quotient amax / 7 once;
+2. the code: with r the fp32 reciprocal of s (correctly rounded, or one ulp
+   off, as the hardware reciprocal), y = fma(w, r, 192) rounds w * r once to
+   the 2^-16 grid of [128, 256), y is clamped to [184, 199], and
+   y + (1.5 * 2^23 + 8 - 192) rounds half to even to an integer whose low
+   byte is q + 8; claimed equal to clamp(round_half_even(w / s), -8, 7).
 
-Here numpy's IEEE fp32 operations replay those steps (every product, quotient
-and rint correctly rounded, as on the GPU), and the results are compared with
-exact arithmetic: float64 values of binary16 numbers and of small multiples
-of them are exact, so the distances below carry no rounding. These tests pin
-the kernel's method, not the oracle.
+Here the fp32 steps are replayed exactly (the rounding of the fused
+multiply-add with integer arithmetic on the significands, the others in
+float64, where these values are exact) and compared with exact arithmetic:
+float64 values of binary16 numbers and of small multiples of them are exact,
+so the distances below carry no rounding. These tests pin the kernel's
+method, not the oracle.
 """
 import numpy as np
 import pytest
@@ -36,10 +39,10 @@ def _f16_neighbours(x):
 
 
 def test_scale_rounding_over_every_binary16_amax():
-    """fp16(fp32(amax) / 7) is the binary16 value nearest to amax / 7 (ties
-    to even) for every finite positive binary16 amax."""
+    """fp16(fp32(amax) * fp32(1/7)) is the binary16 value nearest to
+    amax / 7 (ties to even) for every finite positive binary16 amax."""
     amax = _all_positive_f16()
-    s = (amax.astype(np.float32) / np.float32(7.0)).astype(np.float16).astype(np.float64)
+    s = (amax.astype(np.float32) * np.float32(1.0 / 7.0)).astype(np.float16).astype(np.float64)
     lo, hi = _f16_neighbours(s)
     # compare distances times 7: |amax - 7 v| is exact in float64 (7 v has
     # at most 14 significant bits, amax and 7 v are within 2^17 of each other)
@@ -56,15 +59,41 @@ def test_scale_rounding_over_every_binary16_amax():
     assert not np.any(tie)
 
 
+def _significand(x, bits):
+    """x = sign * m * 2^e with m an integer below 2^bits (x finite, exact)."""
+    f, e = np.frexp(np.abs(x))
+    m = np.round(f * 2.0 ** bits).astype(np.int64)     # exact: x has <= bits significant bits
+    return np.sign(x).astype(np.int64), m, e.astype(np.int64) - bits
+
+
+def _rhe_shift(t, sh):
+    """round_half_even(t * 2^sh) for non-negative int64 t and int64 sh."""
+    up = np.where(sh >= 0, t << np.clip(sh, 0, 62), 0)
+    n = np.clip(-sh, 1, 62)
+    q0 = t >> n
+    rem = t - (q0 << n)
+    half = np.int64(1) << (n - 1)
+    down = q0 + ((rem > half) | ((rem == half) & (q0 % 2 == 1))).astype(np.int64)
+    down = np.where(-sh > 60, 0, down)                   # t < 2^35: far below one half
+    return np.where(sh >= 0, up, down)
+
+
 def _kernel_code(w, s, inv):
     """The kernel's code for weight w with scale s and fp32 reciprocal inv:
-    q = rint(w * inv) in fp32, then moved to the even neighbour when the
-    remainder w - q s is exactly +-s/2 and q is odd; clamped to [-8, 7]."""
-    q = np.rint(w.astype(np.float32) * inv.astype(np.float32)).astype(np.float64)
-    rem = w - q * s                      # exact (q has at most 4 bits)
-    tie = (np.abs(rem) == 0.5 * s) & (np.abs(q) % 2 == 1)
-    q = np.where(tie, q + np.sign(rem), q)
-    return np.clip(q, -8, 7)
+    y = fp32(fma(w, inv, 192)) (one rounding of the exact value to the 2^-16
+    grid), clamped to [184, 199], then rounded half to even to an integer
+    (the fp32 add of 1.5 * 2^23 + 8 - 192); q = that integer - 192."""
+    inv = inv.astype(np.float64)
+    assert np.all(np.abs(w * inv) < 64), "y must stay in [128, 256)"
+    sw, mw, ew = _significand(w, 11)
+    si, mi, ei = _significand(inv, 24)
+    # y * 2^16 = 192 * 2^16 + round_half_even(w * inv * 2^16): adding the
+    # even integer 192 * 2^16 commutes with the rounding
+    r = _rhe_shift(mw * mi, ew + ei + 16) * sw * si
+    y = np.clip(192 * 65536 + r, 184 * 65536, 199 * 65536)
+    base, frac = y >> 16, y & 0xFFFF
+    up = (frac > 0x8000) | ((frac == 0x8000) & (base % 2 == 1))
+    return (base + up.astype(np.int64) - 192).astype(np.float64)
 
 
 def _exact_code(w, s):
@@ -90,8 +119,8 @@ def _reciprocals(s):
 def test_code_rounding_at_and_next_to_every_half_integer(which):
     """For every finite positive binary16 scale s and every half-integer h in
     [-7.5, 7.5]: w = the binary16 values at and next to h s (two neighbours
-    each side), and also at and next to the integer multiples q s. The tie
-    correction must give round_half_even(w / s) exactly."""
+    each side), and also at and next to the integer multiples q s. The
+    snapped rounding must give round_half_even(w / s) exactly."""
     s_all = _all_positive_f16()
     halves = np.arange(-15, 16, 2, dtype=np.float64) / 2.0          # -7.5 ... 7.5
     ints = np.arange(-8, 8, dtype=np.float64)
@@ -135,6 +164,21 @@ def test_code_rounding_random_pairs():
         w = (t * s).astype(np.float16).astype(np.float64)
     keep = np.isfinite(w) & (np.abs(w / s) <= 7.5)
     w, s = w[keep], s[keep]
+    want = _exact_code(w, s)
+    for inv in _reciprocals(s):
+        assert np.array_equal(_kernel_code(w, s, inv), want)
+
+
+def test_code_clamps_past_the_range():
+    """Subnormal scales: fp16(amax / 7) can fall well below amax / 7, so that
+    |w / s| reaches up to 10.5; the clamp of y must give clamp(rhe(w / s))."""
+    rng = np.random.default_rng(7)
+    s = rng.integers(1, 0x0400, 200_000).astype(np.uint16).view(np.float16).astype(np.float64)   # subnormal
+    t = rng.uniform(-10.5, 10.5, s.size)
+    w = (t * s).astype(np.float16).astype(np.float64)
+    keep = np.abs(w / s) <= 10.5
+    w, s = w[keep], s[keep]
+    assert np.any(np.abs(w / s) > 8)
     want = _exact_code(w, s)
     for inv in _reciprocals(s):
         assert np.array_equal(_kernel_code(w, s, inv), want)
