@@ -135,6 +135,7 @@ enum W4A16Cfg {
     W4A16_GEMV_MFMA_NW8 = 17,  // ... K over 8 wavefronts
     W4A16_PC_64x128 = 18,      // slice 64 x 128: 4 producer + 4 consumer wavefronts around a 4-slot LDS ring
     W4A16_PC_64x128_C8 = 19,   // ... 4 producer + 8 consumer wavefronts (64 x 16 each)
+    W4A16_GEMV_MFMA_NW16 = 20, // decode on MFMA (as 16), K over 16 wavefronts of 2 steps each
     W4A16_CFG_COUNT
 };
 

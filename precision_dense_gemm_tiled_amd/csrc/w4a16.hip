@@ -1550,11 +1550,15 @@ static int64_t gemv_mfma_lds(int mm, int nw, int64_t K) {
     return mm * K * 2 + (K / 128) * mm * 4 + (int64_t)nw * mm * 16 * 4;
 }
 
+// Steps whose loads a wavefront issues together: the whole range of a
+// 4096-k row at the workgroup's wavefront count (a larger chunk would only
+// reload the last step into the unused slots).
 template <int NW, int MM, int XPR>
 static hipError_t launch_gemv_mfma_mm(const W4A16Problem &p, hipStream_t stream, int lg) {
+    constexpr int SPW = NW >= 16 ? 2 : (NW >= 8 ? 4 : 8);
     dim3 grid((p.N + 15) / 16, (p.M + MM - 1) / MM);
     const size_t lds = (size_t)gemv_mfma_lds(MM, NW, p.K);
-    hipLaunchKernelGGL((w4a16_gemv_mfma_kernel<NW, MM, 8, XPR>), grid, dim3(NW * 64), lds, stream, p, lg);
+    hipLaunchKernelGGL((w4a16_gemv_mfma_kernel<NW, MM, SPW, XPR>), grid, dim3(NW * 64), lds, stream, p, lg);
     return hipGetLastError();
 }
 
@@ -1567,12 +1571,19 @@ static hipError_t launch_gemv_mfma(const W4A16Problem &p, hipStream_t stream, in
     const int64_t chunks = p.K / 8;
     if (lg < 7 || gemv_mfma_lds(mm, NW, p.K) > GEMV_MFMA_LDS_MAX || chunks > 4 * NW * 64)
         return p.M == 1 ? launch_gemv<2, 2>(p, stream, lg) : launch_gemv<4, 2>(p, stream, lg);
-    const bool x2 = chunks <= 2 * NW * 64;
+    // activation chunks each thread stages: 1, 2 or 4
+    const int xpr = chunks <= NW * 64 ? 1 : (chunks <= 2 * NW * 64 ? 2 : 4);
+    auto go = [&](auto mmc) {
+        constexpr int MMC = decltype(mmc)::value;
+        return xpr == 1   ? launch_gemv_mfma_mm<NW, MMC, 1>(p, stream, lg)
+               : xpr == 2 ? launch_gemv_mfma_mm<NW, MMC, 2>(p, stream, lg)
+                          : launch_gemv_mfma_mm<NW, MMC, 4>(p, stream, lg);
+    };
     if (mm == 1)
-        return x2 ? launch_gemv_mfma_mm<NW, 1, 2>(p, stream, lg) : launch_gemv_mfma_mm<NW, 1, 4>(p, stream, lg);
+        return go(std::integral_constant<int, 1>{});
     if (mm == 2)
-        return x2 ? launch_gemv_mfma_mm<NW, 2, 2>(p, stream, lg) : launch_gemv_mfma_mm<NW, 2, 4>(p, stream, lg);
-    return x2 ? launch_gemv_mfma_mm<NW, 4, 2>(p, stream, lg) : launch_gemv_mfma_mm<NW, 4, 4>(p, stream, lg);
+        return go(std::integral_constant<int, 2>{});
+    return go(std::integral_constant<int, 4>{});
 }
 
 template <int MB, int NB, int WN, int WK, int NST, int PD, int RG>
@@ -1762,7 +1773,8 @@ const char *w4a16_cfg_name(int cfg) {
         "mfma gemv, 16 rows per workgroup, K over 4 wavefronts",
         "mfma gemv, 16 rows per workgroup, K over 8 wavefronts",
         "slice 64 x 128, 4 producer + 4 consumer wavefronts, 4-slot LDS ring",
-        "slice 64 x 128, 4 producer + 8 consumer wavefronts, 4-slot LDS ring"};
+        "slice 64 x 128, 4 producer + 8 consumer wavefronts, 4-slot LDS ring",
+        "mfma gemv, 16 rows per workgroup, K over 16 wavefronts"};
     return cfg >= 0 && cfg < W4A16_CFG_COUNT ? names[cfg] : "?";
 }
 
@@ -1808,6 +1820,7 @@ static hipError_t launch_one(const W4A16Problem &p, const W4A16Plan &plan, const
     case W4A16_GEMV_R8_KS1: return launch_gemv<8, 1>(p, stream, lg);
     case W4A16_GEMV_MFMA_NW4: return launch_gemv_mfma<4>(p, stream, lg);
     case W4A16_GEMV_MFMA_NW8: return launch_gemv_mfma<8>(p, stream, lg);
+    case W4A16_GEMV_MFMA_NW16: return launch_gemv_mfma<16>(p, stream, lg);
 #define MPG_LAUNCH(C, mb, nb, wn, wk, nst, pd, rg) \
     case C: return launch_slice<mb, nb, wn, wk, nst, pd, rg>(p, plan, ws, stream, lg);
         MPG_SLICE_CONFIGS(MPG_LAUNCH)

@@ -387,7 +387,7 @@ def test_w4a16_ragged(M, N, K, G):
     _check_w4(X, W, S, K, G, f"w4a16 {M}x{N}x{K} G={G}")
 
 
-W4A16_CFGS = 20
+W4A16_CFGS = 21
 
 
 @pytest.mark.parametrize("M,N,K,G", [(96, 4096, 4096, 128), (256, 4096, 4096, 128), (512, 4096, 4096, 128),
