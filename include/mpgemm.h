@@ -263,7 +263,9 @@ enum {
  * persistent workgroups of a stream-K launch, which runs the first
  * sk_tiles_dp tiles whole and splits the K loops of the remaining tiles
  * evenly over the grid (the MPGEMM_STREAMK=0/1 override turns it off, or on
- * whenever the tiles do not fill whole waves of the grid).
+ * whenever the tiles do not fill whole waves of the grid; =2 runs every tile
+ * whole on a persistent grid of the resident workgroups, a measured
+ * alternative).
  * mpgemm_plan_w4a16: the configuration of mpgemm_run_w4a16 (the index the
  * MPGEMM_W4A16_CFG override takes), the number of workgroups K is split over
  * (k_splits; 1 = no second reduction kernel) and the K extent of one split. */

@@ -289,6 +289,8 @@ mpgemm_status_t mpgemm_create(mpgemm_handle_t *out, int device) {
             h->streamk_mode = mpg::SK_MODE_OFF;
         else if (env[0] == '1')
             h->streamk_mode = mpg::SK_MODE_ON;
+        else if (env[0] == '2')
+            h->streamk_mode = mpg::SK_MODE_PERSIST;
     }
     // Workspace (partial sums of split K loops, stream-K arrival counters),
     // allocated once here; the counters start at zero and every stream-K

@@ -1418,6 +1418,13 @@ StreamKPlan plan_stream_k(int cfg, int64_t M, int64_t N, int64_t kbytes, int cu_
         return pl;
     const int64_t T = ((M + c.BM - 1) / c.BM) * ((N + c.BN - 1) / c.BN);
     const int64_t G = (int64_t)cu_count * c.per_cu;   // workgroups resident at once
+    if (mode == SK_MODE_PERSIST) {
+        if (T > INT32_MAX)
+            return pl;
+        pl.grid = (int)(T < G ? T : G);
+        pl.tiles_dp = (int)T;
+        return pl;   // sk_tiles = iters = 0
+    }
     const int64_t full = T / G, rem = T % G;
     if (rem == 0)
         return pl;   // whole waves: nothing to balance
@@ -1461,8 +1468,9 @@ static hipError_t launch_one(const GemmProblem &p, const StreamKPlan &sk, const 
     dim3 block(64 * WGM * WGN);
     if (sk.grid > 0) {
         // the plan was made for this tile shape and workspace
+        const bool dp_only = sk.sk_tiles == 0 && sk.iters == 0;   // persistent, every tile whole
         if (sk.tiles_dp + sk.sk_tiles != tiles_m * tiles_n || sk.sk_tiles > ws.flag_count ||
-            2 * (int64_t)sk.grid * BM * BN * 4 > ws.partial_bytes || sk.iters < sk.grid ||
+            (!dp_only && (2 * (int64_t)sk.grid * BM * BN * 4 > ws.partial_bytes || sk.iters < sk.grid)) ||
             sk.iters != (int64_t)sk.sk_tiles * ((p.kbytes + BKB - 1) / BKB))
             return hipErrorInvalidValue;
         StreamKArgs a;

@@ -94,7 +94,9 @@ struct StreamKPlan {
 // Stream-K policy: MODE_AUTO decides by the fill of the last wave of tiles,
 // MODE_OFF never splits, MODE_ON splits whenever the tiles do not fill whole
 // waves of the grid (the ablation override).
-enum StreamKMode { SK_MODE_AUTO = -1, SK_MODE_OFF = 0, SK_MODE_ON = 1 };
+// SK_MODE_PERSIST: the stream-K kernel with every tile whole (a persistent
+// data-parallel grid of the resident workgroups; a measured alternative)
+enum StreamKMode { SK_MODE_AUTO = -1, SK_MODE_OFF = 0, SK_MODE_ON = 1, SK_MODE_PERSIST = 2 };
 StreamKPlan plan_stream_k(int cfg, int64_t M, int64_t N, int64_t kbytes, int cu_count,
                           int64_t partial_bytes, int flag_count, int mode);
 // Transposed-B control: B (the B^T of the K x N layout) rows are k, ldb_b
