@@ -108,6 +108,34 @@ def test_auto_plan_splits_a_long_k(prec, monkeypatch):
         assert np.array_equal(got, dp)
 
 
+@pytest.mark.parametrize("prec", ["i8", "i4", "f16"])
+@pytest.mark.parametrize("M,N,K", [(1100, 1300, 992), (300, 520, 4096), (2048, 2048, 2048)])
+def test_persistent_whole_tiles(prec, M, N, K, monkeypatch):
+    """MPGEMM_STREAMK=2: the stream-K kernel with every tile whole on a
+    persistent grid of the resident workgroups (each loops over several
+    tiles at 1100 x 1300 with 64 x 64 tiles and at 2048^2; fewer tiles than
+    workgroups at 300 x 520), on every tile configuration at 2048^2 and with
+    the default choice otherwise: the oracle's result, and for the integer
+    precisions the one-tile-per-workgroup launch's bit for bit. (FP16 may
+    differ from it in the last bits where a configuration's own kernel is not
+    the ring kernel: the persistent grid always runs the ring kernel.)"""
+    A, B = inputs.gemm_problem(prec, M, N, K, seed=M + N + K)
+    ref = _ref(prec, A, B, K)
+    cfgs = range(N_TILE_CFGS) if M == 2048 else [None]
+    for cfg in cfgs:
+        if cfg is not None:
+            monkeypatch.setenv("MPGEMM_TILE_CFG", str(cfg))
+        monkeypatch.setenv("MPGEMM_STREAMK", "2")
+        with mp.Handle() as h:
+            got = _run(prec, A, B, K, h.value)
+        _compare(prec, got, ref, K, f"{prec} {M}x{N}x{K} cfg {cfg} persistent")
+        if prec != "f16":
+            monkeypatch.setenv("MPGEMM_STREAMK", "0")
+            with mp.Handle() as h:
+                dp = _run(prec, A, B, K, h.value)
+            assert np.array_equal(got, dp), f"{prec} cfg {cfg} persistent vs per-tile"
+
+
 def test_graph_replays_match_eager(monkeypatch):
     """A stream-K launch captured in a HIP graph: every replay (with eager work
     and synchronisation in between) gives the eager result bit for bit."""
