@@ -56,6 +56,7 @@ enum TileCfg {
     CFG_256x256_SC0 = 19,   // (ablation of CFG_256x256_BK128) tile loads with the sc0 cache-policy bit
     CFG_256x256_EARLY = 20, // (ablation of CFG_256x256_BK128) fragment reads fenced ahead of each k-step's MFMAs
     CFG_256x256_WEAVE = 21, // (ablation of CFG_256x256_BK128) fragment reads woven between a k-step's first MFMAs
+    CFG_64x64_DEEP = 22,    // 4 waves of 32x32, BK = 128 B, 8 stages: a short K loop wholly in flight
     CFG_COUNT
 };
 

@@ -9,7 +9,7 @@ import numpy as np
 # VGPR-staged loads, spread loads), 18 the 256 x 256 kernel with B loaded
 # straight into registers, 19 the sc0 cache-policy ablation of the ring, 20
 # the ring with each k-step's fragment reads fenced ahead of its MFMAs.
-N_TILE_CFGS = 22
+N_TILE_CFGS = 23
 PINGPONG_CFG = 12
 B_DIRECT_CFGS = (18,)
 

@@ -26,8 +26,9 @@ def mp():
 @pytest.mark.parametrize("prec", [0, 1, 2, 3])
 def test_tile_config_at_the_workload_sizes(mp, prec):
     """Square sizes of the benchmark on 256 compute units: 64x64 tiles at 512
-    and 1024, 128x128 with a 4-stage ring at 2048, 256x256 from 4096 on."""
-    want = {512: 2, 1024: 2, 2048: 6, 4096: 4, 8192: 4}
+    and 1024 (FP16 at 1024, 16 K stages: the 8-stage ring), 128x128 with a
+    4-stage ring at 2048, 256x256 from 4096 on."""
+    want = {512: 2, 1024: 22 if prec == 0 else 2, 2048: 6, 4096: 4, 8192: 4}
     for n, cfg in want.items():
         # whole waves of tiles (or a grid below one wave): data-parallel
         assert mp.mpgemm_plan_gemm(prec, n, n, n, 256) == (OK, cfg, 0, 0), n
@@ -50,7 +51,7 @@ def test_tile_config_fills_the_compute_units(mp):
 
 # tile configurations: (BM, BN, K bytes per stage, workgroups per compute unit)
 TILE = {0: (256, 256, 64, 1), 1: (128, 128, 64, 2), 2: (64, 64, 128, 3), 3: (256, 128, 128, 1),
-        4: (256, 256, 128, 1), 5: (128, 256, 128, 1), 6: (128, 128, 128, 1)}
+        4: (256, 256, 128, 1), 5: (128, 256, 128, 1), 6: (128, 128, 128, 1), 22: (64, 64, 128, 1)}
 KBYTES = {0: lambda K: 2 * K, 1: lambda K: K, 2: lambda K: K // 2, 3: lambda K: K // 2}
 WORKSPACE_BYTES = 128 << 20
 
