@@ -324,29 +324,37 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(W4A16Problem p, int lg)
 
     const NibbleConsts nk = nibble_consts();
     for (int c = c_begin + lane; c < c_end; c += 64) {
+        // activations first, then scales and weight rows: the pairing and
+        // the offset term (activations only) and the first rows' products
+        // run while the later loads are still in flight
         i32x4 wv[R];
         uint16_t sv[R];
         i32x4 xv[MM][4];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            wv[r] = *reinterpret_cast<const i32x4 *>(wrow[r] + 16u * (uint32_t)c);
-            sv[r] = srow[r][(uint32_t)(32 * c) >> lg];
-        }
 #pragma unroll
         for (int mm = 0; mm < MM; ++mm)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
                 xv[mm][t] = reinterpret_cast<const i32x4 *>(xrow[mm] + 32u * (uint32_t)c)[t];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            sv[r] = srow[r][(uint32_t)(32 * c) >> lg];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            wv[r] = *reinterpret_cast<const i32x4 *>(wrow[r] + 16u * (uint32_t)c);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mm = 0; mm < MM; ++mm) {
             uint32_t xp[16];
             pair_x(xv[mm], xp);
             const float off = offset_of_chunk(xp);
+            // (scheduling fences: each row's products wait only for its own
+            // weight load, not for the last one)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const float s = (float)__builtin_bit_cast(_Float16, sv[r]);
                 acc[mm][r] += (dot_chunk(wv[r], xp, nk) - off) * s;
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
