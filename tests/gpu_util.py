@@ -38,6 +38,15 @@ def f16_tol(K: int) -> float:
     return 2.0 ** -10 * math.sqrt(max(K, 1))
 
 
+def w4a4_tol(y, c_abs, sx, sw, b):
+    """W4A4 bar: fp16 output rounding (half an ulp: 2^-11 relative) plus the
+    fp32 epilogue (two products and one sum, each within 2^-24 relative) plus
+    subnormals; c_abs = |exact integer product|."""
+    mag = c_abs * np.abs(sx.astype(np.float64))[:, None] * np.abs(sw.astype(np.float64))[None, :]
+    bb = np.abs(b.astype(np.float64))[None, :] if b is not None else 0.0
+    return 2.0 ** -11 * np.abs(y) + 3 * 2.0 ** -24 * (mag + bb) + 2.0 ** -24
+
+
 def w4a16_tol(y_ref: np.ndarray, t2: np.ndarray, K: int) -> np.ndarray:
     """W4A16 bar: half an fp16 ulp of the output, plus fp16 dequantisation
     rounding of each term (relative 2^-11, random sign, summed over K terms of

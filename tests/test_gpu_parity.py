@@ -13,7 +13,7 @@ import oracle
 import precision_dense_gemm_tiled_amd as mp
 from precision_dense_gemm_tiled_amd import inputs
 from tests.gpu_util import (B_DIRECT_CFGS, N_TILE_CFGS, PINGPONG_CFG, band_rows, dev, f16_tol, freivalds_int, host,
-                            pack_i4, require_gpu, unpack_i4, w4a16_tol)
+                            pack_i4, require_gpu, unpack_i4, w4a4_tol, w4a16_tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -497,14 +497,6 @@ def test_w4a16_strided(M, N, K, G, cfg, monkeypatch):
 
 
 # ------------------------------------------------------------------ W4A4: INT4 x INT4 with scale epilogue
-
-def w4a4_tol(y, c_abs, sx, sw, b):
-    """fp16 output rounding (half an ulp: 2^-11 relative) plus the fp32 epilogue
-    (two products and one sum, each within 2^-24 relative) plus subnormals."""
-    mag = c_abs * np.abs(sx.astype(np.float64))[:, None] * np.abs(sw.astype(np.float64))[None, :]
-    bb = np.abs(b.astype(np.float64))[None, :] if b is not None else 0.0
-    return 2.0 ** -11 * np.abs(y) + 3 * 2.0 ** -24 * (mag + bb) + 2.0 ** -24
-
 
 def _w4a4_check(A, B, K, sx, sw, b, got, what):
     y = oracle.gemm_w4a4(A, B, K, sx, sw, b)
