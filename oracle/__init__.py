@@ -44,6 +44,8 @@ def lib():
         L.oracle_gemm_w4a16.restype = ctypes.c_int
         L.oracle_gemm_w4a4.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _p, _i64]
         L.oracle_gemm_w4a4.restype = ctypes.c_int
+        L.oracle_w4a4_lowrank.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64]
+        L.oracle_w4a4_lowrank.restype = ctypes.c_int
         L.oracle_quantize_w4.argtypes = [_i64, _i64, _p, _i64, _i64, _p, _i64, _p, _i64]
         L.oracle_quantize_w4.restype = ctypes.c_int
         L.oracle_threads.argtypes = []
@@ -196,3 +198,25 @@ def gemm_w4a4(Ap, Bp, K, SX, SW, BIAS=None):
     if st != OK:
         raise ValueError(f"oracle_gemm_w4a4 status {st}")
     return Y
+
+
+def w4a4_lowrank(X, LD, LU):
+    """The low-rank branch of the W4A4 formula: U = X LD^T (M x R, double) and
+    L = binary16_rne(U) LU^T (M x N, double, unrounded), for fp16 X (M x K),
+    LD (R x K) and LU (N x R). Returns (U, L)."""
+    def bits(v):
+        v = np.asarray(v)
+        return v.view(np.uint16) if v.dtype == np.float16 else v
+    X, ldx = _rows(bits(X), np.uint16)
+    LD, ldd = _rows(bits(LD), np.uint16)
+    LU, ldu = _rows(bits(LU), np.uint16)
+    M, K = X.shape
+    R, N = LD.shape[0], LU.shape[0]
+    assert LD.shape[1] == K and LU.shape[1] == R, "shapes"
+    U = np.zeros((M, R), dtype=np.float64)
+    L = np.zeros((M, N), dtype=np.float64)
+    st = lib().oracle_w4a4_lowrank(M, N, K, R, _ptr(X), ldx, _ptr(LD), ldd, _ptr(LU), ldu,
+                                   _ptr(U), max(R, 1), _ptr(L), max(N, 1))
+    if st != OK:
+        raise ValueError(f"oracle_w4a4_lowrank status {st}")
+    return U, L

@@ -256,6 +256,37 @@ int oracle_gemm_w4a4(int64_t M, int64_t N, int64_t K,
     return ORACLE_OK;
 }
 
+int oracle_w4a4_lowrank(int64_t M, int64_t N, int64_t K, int64_t R,
+                        const uint16_t *X, int64_t ldx, const uint16_t *LD, int64_t ldd,
+                        const uint16_t *LU, int64_t ldu, double *U, int64_t ldU,
+                        double *L, int64_t ldl)
+{
+    if (M < 0 || N < 0 || K < 0 || R < 0)
+        return ORACLE_ERR_ARG;
+    if (M == 0 || N == 0 || R == 0)
+        return ORACLE_OK;
+    if (!X || !LD || !LU || !U || !L || ldx < K || ldd < K || ldu < R || ldU < R || ldl < N)
+        return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; ++m) {
+        /* step 1: the down-projection of the row, U[m][r] = sum_k X[m][k] LD[r][k] */
+        for (int64_t r = 0; r < R; ++r) {
+            double u = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                u += oracle_f16_decode(X[m * ldx + k]) * oracle_f16_decode(LD[r * ldd + k]);
+            U[m * ldU + r] = u;
+        }
+        /* step 2: the up-projection of U rounded to binary16 (nearest even) */
+        for (int64_t n = 0; n < N; ++n) {
+            double l = 0.0;
+            for (int64_t r = 0; r < R; ++r)
+                l += oracle_f16_decode(oracle_f16_encode_rne(U[m * ldU + r])) * oracle_f16_decode(LU[n * ldu + r]);
+            L[m * ldl + n] = l;
+        }
+    }
+    return ORACLE_OK;
+}
+
 int oracle_quantize_w4(int64_t N, int64_t K, const uint16_t *W, int64_t ldw, int64_t G,
                        uint8_t *Q, int64_t ldq, uint16_t *S, int64_t lds)
 {

@@ -93,11 +93,27 @@ int oracle_gemm_w4a16(int64_t M, int64_t N, int64_t K,
  * the exact integer product; BIAS (N values, may be NULL) added per column:
  *   Y[m][n] = (sum_k qa(m,k) qb(n,k)) * SX[m] * SW[n] + BIAS[n]
  * in double, unrounded (the tests round to fp16 where they compare). A, B
- * packed as for oracle_gemm_i4. The low-rank branch L(X) is not part of it. */
+ * packed as for oracle_gemm_i4. The low-rank branch L(X) is oracle_w4a4_lowrank. */
 int oracle_gemm_w4a4(int64_t M, int64_t N, int64_t K,
                      const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
                      const uint16_t *SX, const uint16_t *SW, const uint16_t *BIAS,
                      double *Y, int64_t ldy);
+
+/* The low-rank residual branch L(X) of the W4A4 formula ("Warp-Specialized
+ * Kernel Implementation for W4A4 MatMul on Latest GPU Architectures",
+ * section 1: Y = (Q(X) Q(W)^T) (.) scale + L(X) + b; the page names a small
+ * down- and up-projection pair and no precision, the reading used is):
+ *   U[m][r] = sum_k X[m][k] LD[r][k]                (the unquantised fp16 input)
+ *   L[m][n] = sum_r binary16_rne(U[m][r]) LU[n][r]  (U enters the second product as fp16)
+ * X: M x K binary16 (row stride ldx), LD: R x K binary16 (the down-projection,
+ * K-contiguous like a weight), LU: N x R binary16 (the up-projection, row
+ * stride ldu). U (M x R) and L (M x N) in double, unrounded; U's sums are
+ * double sums of exact products. The full W4A4 output is oracle_gemm_w4a4's
+ * value plus L. */
+int oracle_w4a4_lowrank(int64_t M, int64_t N, int64_t K, int64_t R,
+                        const uint16_t *X, int64_t ldx, const uint16_t *LD, int64_t ldd,
+                        const uint16_t *LU, int64_t ldu, double *U, int64_t ldU,
+                        double *L, int64_t ldl);
 
 /* Symmetric round-to-nearest INT4 quantisation of fp16 weights per
  * (row, G-wide K group), the step that produces the inputs of

@@ -65,6 +65,15 @@ MUTANTS = [
     ("w4a4 column factor of column 0",
      "double y = (double)acc * sx * oracle_f16_decode(SW[n]);",
      "double y = (double)acc * sx * oracle_f16_decode(SW[0]);", 0),
+    ("low-rank U not rounded to fp16",
+     "l += oracle_f16_decode(oracle_f16_encode_rne(U[m * ldU + r])) * oracle_f16_decode(LU[n * ldu + r]);",
+     "l += U[m * ldU + r] * oracle_f16_decode(LU[n * ldu + r]);", 0),
+    ("low-rank down-projection row 0 for every r",
+     "* oracle_f16_decode(LD[r * ldd + k]);", "* oracle_f16_decode(LD[k]);", 0),
+    ("low-rank up-projection column 0 for every r",
+     "* oracle_f16_decode(LU[n * ldu + r]);", "* oracle_f16_decode(LU[n * ldu]);", 0),
+    ("low-rank drops the last k term",
+     "for (int64_t k = 0; k < K; ++k)\n                u += ", "for (int64_t k = 0; k < K - 1; ++k)\n                u += ", 0),
     ("quantiser scale amax / 8",
      "oracle_f16_encode_rne(amax / 7.0)", "oracle_f16_encode_rne(amax / 8.0)", 0),
     ("quantiser rounds ties away from zero",

@@ -493,3 +493,82 @@ def test_w4a4_scales_and_bias_are_outer_product_and_column_shift(oracle_lib):
     y = oracle_lib.gemm_w4a4(Ap, Bp, K, sx, sw, b)
     want = c * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] + b.astype(np.float64)[None, :]
     assert np.array_equal(y, want)
+
+
+# ------------------------------------------------------------------ W4A4 low-rank branch L(X)
+
+def test_w4a4_lowrank_golden_worked_example(oracle_lib):
+    """The whole W4A4 formula with its low-rank branch on the hand-worked
+    fixture: U, L and the fp16 output."""
+    g = read_golden("w4a4_lowrank_1x2.txt")
+    K = int(g["K"][0][0])
+
+    def f(rows):
+        return np.array([[float(v) for v in r] for r in rows])
+
+    qa = [[int(v) for v in g["QA"][0]]]
+    qb = [[int(v) for v in r] for r in g["QB"]]
+    sx, sw, b = (f(g[k])[0].astype(np.float16) for k in ("SX", "SW", "BIAS"))
+    X, LD, LU = (f(g[k]).astype(np.float16) for k in ("X", "LD", "LU"))
+    U, L = oracle_lib.w4a4_lowrank(X, LD, LU)
+    assert U.tolist() == f(g["U"]).tolist() and L.tolist() == f(g["L"]).tolist()
+    y = oracle_lib.gemm_w4a4(_pack(qa), _pack(qb), K, sx, sw, b) + L
+    assert y.tolist() == f(g["Y"]).tolist()
+    assert [oracle_lib.f16_encode_rne(v) for v in y[0]] == [int(v, 16) for v in g["YBITS"][0]]
+
+
+def test_w4a4_lowrank_rounds_u_to_fp16_nearest_even(oracle_lib):
+    """U enters the up-projection rounded to fp16: U = 1 + 2^-10 + 2^-11 lies
+    halfway between 1 + 2^-10 (odd significand) and 1 + 2^-9 (even), so it
+    becomes 1 + 2^-9; U = (1 + 2^-10)^2 = 1 + 2^-9 + 2^-20 rounds down to
+    1 + 2^-9; an unrounded U would give other values."""
+    X = np.array([[1, 1]], np.float16)
+    LD = np.array([[1 + 2 ** -10, 2 ** -11]], np.float16)
+    U, L = oracle_lib.w4a4_lowrank(X, LD, np.array([[1], [-2]], np.float16))
+    assert U[0, 0] == 1 + 2 ** -10 + 2 ** -11
+    assert L.tolist() == [[1 + 2 ** -9, -2 - 2 ** -8]]
+    X = np.array([[1 + 2 ** -10]], np.float16)
+    U, L = oracle_lib.w4a4_lowrank(X, X, np.array([[1]], np.float16))
+    assert U[0, 0] == 1 + 2 ** -9 + 2 ** -20 and L[0, 0] == 1 + 2 ** -9
+
+
+def test_w4a4_lowrank_brute_force_rationals(oracle_lib):
+    """Tiny random cases against a pure-Python evaluation in exact rationals
+    (fractions), with the fp16 rounding of U done by numpy."""
+    from fractions import Fraction
+    r = rng(31)
+    for M, N, K, R in [(1, 1, 1, 1), (2, 3, 5, 2), (3, 2, 7, 4), (4, 5, 3, 3)]:
+        X = rand_f16(r, (M, K), -2, 2)
+        LD = rand_f16(r, (R, K), -1, 1)
+        LU = rand_f16(r, (N, R), -1, 1)
+        U, L = oracle_lib.w4a4_lowrank(X, LD, LU)
+        for m in range(M):
+            for q in range(R):
+                u = sum(Fraction(float(X[m, k])) * Fraction(float(LD[q, k])) for k in range(K))
+                assert abs(Fraction(U[m, q]) - u) <= abs(u) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+            for n in range(N):
+                want = sum(Fraction(float(np.float16(U[m, q]))) * Fraction(float(LU[n, q])) for q in range(R))
+                assert Fraction(L[m, n]) == want
+
+
+def test_w4a4_lowrank_closed_forms(oracle_lib):
+    """A one-hot down-projection picks input columns (U = X[:, c], exact), so
+    L = X[:, c] times the up-projection: a sum of outer products; a zero
+    up-projection gives L = 0; each row of L depends only on its row of X."""
+    r = rng(32)
+    M, N, K, R = 6, 9, 40, 3
+    X = rand_f16(r, (M, K), -4, 4)
+    LD = np.zeros((R, K), np.float16)
+    cols = [5, 0, 39]
+    for q, c in enumerate(cols):
+        LD[q, c] = 1
+    LU = rand_f16(r, (N, R))
+    U, L = oracle_lib.w4a4_lowrank(X, LD, LU)
+    assert np.array_equal(U, X[:, cols].astype(np.float64))
+    assert np.allclose(L, X[:, cols].astype(np.float64) @ LU.astype(np.float64).T, rtol=0, atol=1e-12)
+    _, Z = oracle_lib.w4a4_lowrank(X, rand_f16(r, (R, K)), np.zeros((N, R), np.float16))
+    assert not np.any(Z)
+    X2 = X.copy()
+    X2[2] = rand_f16(r, (K,))
+    _, L2 = oracle_lib.w4a4_lowrank(X2, LD, LU)
+    assert np.array_equal(np.delete(L2, 2, 0), np.delete(L, 2, 0)) and not np.array_equal(L2[2], L[2])
