@@ -7,7 +7,8 @@ workload at its largest size) with inputs resident in HBM; `value` is its
 throughput. The same run also measures every precision at every size of the
 workloads (FP16/INT8/INT4 square N = 512 ... 8192, W4A16 4096 x 4096 at
 M = 1, 16, 128), the INT4 x INT4 GEMM with scale epilogue (W4A4) at N = 4096
-and 8192, the INT4 weight quantiser at N = K = 4096 and 8192 (G = 128),
+and 8192, the same with its rank-32 low-rank branch (w4a4lr), the INT4 weight
+quantiser at N = K = 4096 and 8192 (G = 128),
 and one pass of the whole GEMM hot path (all of those GEMMs at their largest
 size), reported under `per_precision` and `hot_path`.
 
@@ -19,7 +20,7 @@ entries also carry `us_warm`, the same launches on a single input set that
 stays cached (context only: every throughput and roofline figure is cold).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep]
-                       [--no-cpu-baseline] [--only f16|i8|i4|w4a16|w4a4|quantize] [--eager]
+                       [--no-cpu-baseline] [--only f16|i8|i4|w4a16|w4a4|w4a4lr|quantize] [--eager]
 """
 import argparse
 import hashlib
@@ -37,7 +38,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # MI355X published dense peaks (no sparsity) and HBM bandwidth.
-PEAK = {"f16": 2500.0, "i8": 5000.0, "i4": 5000.0, "w4a4": 5000.0}   # TFLOP/s or TOP/s; INT4 runs on i8 MFMA
+PEAK = {"f16": 2500.0, "i8": 5000.0, "i4": 5000.0, "w4a4": 5000.0,   # TFLOP/s or TOP/s; INT4 runs on i8 MFMA
+        "w4a4lr": 5000.0}   # W4A4 with the low-rank branch: priced as its INT4 product
 HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
@@ -45,8 +47,9 @@ SQUARE_SIZES = [512, 1024, 2048, 4096, 8192]
 W4A16_M = [1, 16, 128]
 W4A16_NK = 4096
 W4A16_G = 128
-CONFIG_INDEX = {"i8_512": 0, "f16": 1, "i8": 2, "i4": 3, "w4a16": 4, "quantize": 5, "w4a4": 6}
+CONFIG_INDEX = {"i8_512": 0, "f16": 1, "i8": 2, "i4": 3, "w4a16": 4, "quantize": 5, "w4a4": 6, "w4a4lr": 7}
 W4A4_SIZES = [4096, 8192]
+LOWRANK_R = 32   # rank of the W4A4 low-rank branch in the sweep
 QUANT_NK = [4096, 8192]   # N = K of the weight matrices quantised (G = 128)
 
 
@@ -107,6 +110,8 @@ def algorithmic_bytes(prec, M, N, K, G=W4A16_G):
         return 2 * M * K + N * K // 2 + 2 * N * (K // G) + 2 * M * N
     if prec == "w4a4":       # packed A and B, fp16 scales and bias, fp16 Y
         return (M * K + N * K) // 2 + 2 * M * N + 2 * M + 4 * N
+    if prec == "w4a4lr":     # the same plus fp16 X, LD (R x K) and LU (N x R)
+        return algorithmic_bytes("w4a4", M, N, K) + 2 * M * K + 2 * LOWRANK_R * (K + N)
     if prec == "quantize":   # read fp16 W, write packed codes and scales
         return 2 * N * K + N * K // 2 + 2 * N * (K // G)
     raise ValueError(prec)
@@ -145,9 +150,12 @@ class Problem:
         from precision_dense_gemm_tiled_amd import inputs
         self.prec, self.M, self.N, self.K = prec, M, N, K
         self.b_layout = b_layout
-        if prec == "w4a4":
-            A, B, SX, SW, BI = inputs.w4a4_problem(M, N, K, seed)
-            t = [torch.from_numpy(v).cuda() for v in (A, B, SX, SW, BI)]
+        if prec in ("w4a4", "w4a4lr"):
+            if prec == "w4a4":
+                vals = inputs.w4a4_problem(M, N, K, seed)
+            else:
+                vals = inputs.w4a4_lowrank_problem(M, N, K, LOWRANK_R, seed)
+            t = [torch.from_numpy(v).cuda() for v in vals]
             self.ins = [tuple(t)] + [tuple(v.clone() for v in t) for _ in range(copies - 1)]
             self.out = torch.empty((M, N), dtype=torch.float16, device="cuda")
         elif prec == "quantize":
@@ -190,6 +198,9 @@ class Problem:
             mp.quantize_w4(ins, W4A16_G, out_q=self.out[0], out_s=self.out[1])
         elif self.prec == "w4a4":
             mp.gemm_w4a4(ins[0], ins[1], self.K, ins[2], ins[3], ins[4], out=self.out)
+        elif self.prec == "w4a4lr":
+            mp.gemm_w4a4_lowrank(ins[0], ins[1], self.K, ins[2], ins[3], ins[5], ins[6], ins[7], bias=ins[4],
+                                 out=self.out)
         else:
             mp.gemm_w4a16(ins[0], ins[1], ins[2], W4A16_G, out=self.out)
 
@@ -503,7 +514,7 @@ def main():
                          "ramps up over ~0.1 s of MFMA work); 0 disables")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["f16", "i8", "i4", "w4a16", "w4a4", "quantize"], default=None,
+    ap.add_argument("--only", choices=["f16", "i8", "i4", "w4a16", "w4a4", "w4a4lr", "quantize"], default=None,
                     help="time only this precision's sweep (no headline line)")
     ap.add_argument("--sizes", type=str, default=None,
                     help="with --only: comma-separated sizes (N, or M for w4a16)")
@@ -548,7 +559,7 @@ def main():
         precs = [args.only]
         out = {}
         for prec in precs:
-            sizes = {"w4a16": W4A16_M, "quantize": QUANT_NK, "w4a4": W4A4_SIZES}.get(prec, SQUARE_SIZES)
+            sizes = {"w4a16": W4A16_M, "quantize": QUANT_NK, "w4a4": W4A4_SIZES, "w4a4lr": W4A4_SIZES}.get(prec, SQUARE_SIZES)
             if args.sizes:
                 sizes = [int(v) for v in args.sizes.split(",")]
             out[prec] = []
@@ -574,8 +585,8 @@ def main():
     extra = {}
     if not args.no_sweep:
         per = {}
-        for prec in ["f16", "i8", "i4", "w4a16", "w4a4", "quantize"]:
-            sizes = {"w4a16": W4A16_M, "quantize": QUANT_NK, "w4a4": W4A4_SIZES}.get(prec, SQUARE_SIZES)
+        for prec in ["f16", "i8", "i4", "w4a16", "w4a4", "w4a4lr", "quantize"]:
+            sizes = {"w4a16": W4A16_M, "quantize": QUANT_NK, "w4a4": W4A4_SIZES, "w4a4lr": W4A4_SIZES}.get(prec, SQUARE_SIZES)
             per[prec] = []
             for s in sizes:
                 M, N, K = (s, W4A16_NK, W4A16_NK) if prec == "w4a16" else ((1, s, s) if prec == "quantize" else (s, s, s))

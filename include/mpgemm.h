@@ -153,18 +153,48 @@ mpgemm_status_t mpgemm_run_i4_kn(mpgemm_handle_t h, int64_t M, int64_t N, int64_
  * Y = (Q(X) Q(W)^T) (.) scale + b with 4-bit activations and weights; the
  * page gives no scale layout, the reading used is one factor per activation
  * row and one per weight row, applied to the exact integer product, and a
- * bias per output column; the low-rank branch L(X) is not part of it):
+ * bias per output column; the low-rank branch L(X) is left to the next call):
  *   Y[m][n] = fp16( (sum_k qa(m, k) qb(n, k)) * SX[m] * SW[n] + bias[n] )
  * A, B: packed signed INT4 exactly as for mpgemm_run_i4 (K, lda, ldb even,
  * K <= MPGEMM_MAX_K_INT). SX: M binary16, SW: N binary16, bias: N binary16 or
  * NULL (no bias); all 2-byte aligned. Y: M x N binary16, row stride ldy.
  * The integer sum is exact; the two products and the bias are applied in
- * fp32 (each correctly rounded), then one rounding to fp16 (nearest even). */
+ * fp32 (each correctly rounded), then one rounding to fp16 (nearest even).
+ * The low-rank branch L(X) is mpgemm_run_w4a4_lowrank. */
 mpgemm_status_t mpgemm_run_w4a4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
                                 const uint8_t *A, int64_t lda,
                                 const uint8_t *B, int64_t ldb,
                                 const uint16_t *SX, const uint16_t *SW, const uint16_t *bias,
                                 uint16_t *Y, int64_t ldy, void *stream);
+
+/* W4A4 with the formula's low-rank residual branch ("Warp-Specialized Kernel
+ * Implementation for W4A4 MatMul on Latest GPU Architectures", section 1:
+ * Y = (Q(X) Q(W)^T) (.) scale + L(X) + b, L a small down- and up-projection
+ * of the unquantised input; the page fixes no precision, the reading used is
+ * fp16 operands with fp32 sums and the projected activations rounded to fp16
+ * before the up-projection):
+ *   U[m][r] = sum_k X[m][k] LD[r][k]                        (fp32 sum)
+ *   L[m][n] = sum_r fp16_rne(U[m][r]) LU[n][r]               (fp32 sum)
+ *   Y[m][n] = fp16( (((sum_k qa qb) * SX[m]) * SW[n] + L[m][n]) + bias[n] )
+ * A, B, SX, SW, bias, Y: exactly as for mpgemm_run_w4a4.
+ * X:  M x K binary16, the unquantised activations, row stride ldx >= K.
+ * LD: R x K binary16, the down-projection (K-contiguous), row stride ldd >= K.
+ * LU: N x R binary16, the up-projection (R-contiguous), row stride ldu >= R.
+ * R must be a multiple of 16 with R <= MPGEMM_MAX_LOWRANK, LU 16-byte aligned
+ * with ldu a multiple of 8, X and LD 2-byte aligned (else
+ * MPGEMM_ERR_UNSUPPORTED); R == 0 is mpgemm_run_w4a4. U lives in the
+ * handle's workspace: M * R * 4 bytes (rounded up to 256) may take at most
+ * half of it, else MPGEMM_ERR_UNSUPPORTED. Two launches on `stream`: U by the
+ * FP16 tile kernel, then the W4A4 tile kernel, whose epilogue adds L per
+ * 32 x 32 output block on the matrix unit. The fp32 sums' order is
+ * unspecified; every other step rounds as written. */
+#define MPGEMM_MAX_LOWRANK 256
+mpgemm_status_t mpgemm_run_w4a4_lowrank(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                        const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                                        const uint16_t *SX, const uint16_t *SW, const uint16_t *bias,
+                                        const uint16_t *X, int64_t ldx, const uint16_t *LD, int64_t ldd,
+                                        const uint16_t *LU, int64_t ldu, int64_t R,
+                                        uint16_t *Y, int64_t ldy, void *stream);
 
 /* Weight-only INT4 GEMM ("fused-int4-gemm-sm75" README: register
  * dequantisation, per-group scales with group_size = 128; decode M = 1 and

@@ -14,10 +14,10 @@ __all__ = [
     "MpgemmError", "lib", "lib_path",
     "mpgemm_create", "mpgemm_destroy", "mpgemm_status_string",
     "mpgemm_run_f16", "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_run_w4a4", "mpgemm_quantize_w4",
-    "mpgemm_run_w4a16_noalloc", "mpgemm_stream_read",
+    "mpgemm_run_w4a4_lowrank", "mpgemm_run_w4a16_noalloc", "mpgemm_stream_read",
     "mpgemm_run_f16_kn", "mpgemm_run_i8_kn", "mpgemm_run_i4_kn",
     "mpgemm_plan_gemm", "mpgemm_plan_w4a16",
-    "Handle", "default_handle", "gemm_f16", "gemm_i8", "gemm_i4", "gemm_w4a16", "gemm_w4a4", "quantize_w4",
+    "Handle", "default_handle", "gemm_f16", "gemm_i8", "gemm_i4", "gemm_w4a16", "gemm_w4a4", "gemm_w4a4_lowrank", "quantize_w4",
     "gemm_w4a16_noalloc",
     "gemm_f16_kn", "gemm_i8_kn", "gemm_i4_kn",
 ]
@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.mpgemm_run_w4a4.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
                                       _vp, _i64, _vp]
         L.mpgemm_run_w4a4.restype = ctypes.c_int
+        L.mpgemm_run_w4a4_lowrank.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
+                                              _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp]
+        L.mpgemm_run_w4a4_lowrank.restype = ctypes.c_int
         L.mpgemm_plan_gemm.argtypes = [ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
         L.mpgemm_plan_gemm.restype = ctypes.c_int
@@ -139,6 +142,12 @@ def mpgemm_run_w4a16_noalloc(M, N, K, X, ldx, Wq, ldw, S, lds, group_size, Y, ld
 
 def mpgemm_run_w4a4(h, M, N, K, A, lda, B, ldb, SX, SW, bias, Y, ldy, stream=None) -> int:
     return lib().mpgemm_run_w4a4(h, M, N, K, A, lda, B, ldb, SX, SW, bias, Y, ldy, stream)
+
+
+def mpgemm_run_w4a4_lowrank(h, M, N, K, A, lda, B, ldb, SX, SW, bias, X, ldx, LD, ldd, LU, ldu, R, Y, ldy,
+                            stream=None) -> int:
+    return lib().mpgemm_run_w4a4_lowrank(h, M, N, K, A, lda, B, ldb, SX, SW, bias, X, ldx, LD, ldd, LU, ldu, R,
+                                         Y, ldy, stream)
 
 
 def mpgemm_plan_gemm(precision, M, N, K, cu_count=256):
@@ -395,4 +404,31 @@ def gemm_w4a4(A, B, K, sx, sw, bias=None, out=None, handle=None, stream=None):
     _check(mpgemm_run_w4a4(h, M, N, K, A.data_ptr(), 2 * lda_b, B.data_ptr(), 2 * ldb_b, sx.data_ptr(),
                            sw.data_ptr(), bias.data_ptr() if bias is not None else None, Y.data_ptr(), ldy,
                            _stream(stream)), "mpgemm_run_w4a4")
+    return Y
+
+
+def gemm_w4a4_lowrank(A, B, K, sx, sw, X, LD, LU, bias=None, out=None, handle=None, stream=None):
+    """gemm_w4a4 plus the low-rank branch: Y = fp16(((A_int4 @ B_int4.T) *
+    sx[:, None] * sw[None, :] + fp16(X @ LD.T) @ LU.T) + bias), with fp16 X
+    (M x K, the unquantised activations), LD (R x K) and LU (N x R)."""
+    import torch
+    lda_b = _rows(A, torch.uint8, "A")
+    ldb_b = _rows(B, torch.uint8, "B")
+    ldx = _rows(X, torch.float16, "X")
+    ldd = _rows(LD, torch.float16, "LD")
+    ldu = _rows(LU, torch.float16, "LU")
+    M, N, R = A.shape[0], B.shape[0], LD.shape[0]
+    if X.shape != (M, K) or LD.shape[1] != K or LU.shape != (N, R):
+        raise ValueError(f"shapes: X {tuple(X.shape)}, LD {tuple(LD.shape)}, LU {tuple(LU.shape)} for "
+                         f"M = {M}, N = {N}, K = {K}")
+    for name, v, n in (("sx", sx, M), ("sw", sw, N)) + ((("bias", bias, N),) if bias is not None else ()):
+        if v.dtype != torch.float16 or v.numel() != n or not v.is_contiguous() or not v.is_cuda:
+            raise ValueError(f"{name}: expected {n} contiguous fp16 values on the device")
+    Y = torch.empty((M, N), dtype=torch.float16, device=A.device) if out is None else out
+    ldy = _rows(Y, torch.float16, "Y")
+    h = default_handle(A.device.index) if handle is None else handle
+    _check(mpgemm_run_w4a4_lowrank(h, M, N, K, A.data_ptr(), 2 * lda_b, B.data_ptr(), 2 * ldb_b, sx.data_ptr(),
+                                   sw.data_ptr(), bias.data_ptr() if bias is not None else None, X.data_ptr(),
+                                   ldx, LD.data_ptr(), ldd, LU.data_ptr(), ldu, R, Y.data_ptr(), ldy,
+                                   _stream(stream)), "mpgemm_run_w4a4_lowrank")
     return Y

@@ -99,10 +99,19 @@ struct DeviceGuard {
     }
 };
 
+// The low-rank branch of a W4A4 call: U (fp32, M x rank) and the up-projection.
+struct LowRankArgs {
+    const float *u;
+    const uint16_t *v;
+    int64_t ldu, ldv;
+    int rank;
+};
+
 mpgemm_status_t run_tile(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int64_t kbytes,
                          const void *A, int64_t lda_b, const void *B, int64_t ldb_b, void *C,
                          int64_t ldc, void *stream, const uint16_t *sx = nullptr,
-                         const uint16_t *sw = nullptr, const uint16_t *bias = nullptr) {
+                         const uint16_t *sw = nullptr, const uint16_t *bias = nullptr,
+                         const LowRankArgs *lr = nullptr, const mpg::TileWorkspace *ws = nullptr) {
     DeviceGuard dg(h->device);
     if (!dg.ok)
         return MPGEMM_ERR_HIP;
@@ -120,12 +129,20 @@ mpgemm_status_t run_tile(mpgemm_handle_t h, int prec, int64_t M, int64_t N, int6
     p.sw = sw;
     p.bias = bias;
     p.c_vec16 = (reinterpret_cast<uintptr_t>(C) % 16 == 0 && ldc % 4 == 0) ? 1 : 0;
+    if (lr) {
+        p.lr_u = lr->u;
+        p.lr_v = lr->v;
+        p.lr_ldu = lr->ldu;
+        p.lr_ldv = lr->ldv;
+        p.lr_rank = lr->rank;
+    }
+    const mpg::TileWorkspace &tws = ws ? *ws : h->tile_ws;
     int cfg = h->forced_tile_cfg >= 0 ? h->forced_tile_cfg
                                       : mpg::choose_tile_cfg(prec, M, N, kbytes, h->cu_count);
     const mpg::StreamKPlan sk =
-        mpg::plan_stream_k(cfg, M, N, kbytes, h->cu_count, h->tile_ws.partial_bytes,
-                           h->tile_ws.flag_count, h->streamk_mode);
-    hipError_t e = mpg::launch_gemm(prec, cfg, p, sk, h->tile_ws, static_cast<hipStream_t>(stream));
+        mpg::plan_stream_k(cfg, M, N, kbytes, h->cu_count, tws.partial_bytes, tws.flag_count,
+                           h->streamk_mode);
+    hipError_t e = mpg::launch_gemm(prec, cfg, p, sk, tws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MPGEMM_OK : MPGEMM_ERR_HIP;
 }
 
@@ -433,6 +450,51 @@ mpgemm_status_t mpgemm_run_w4a4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t
     if (!h)
         return MPGEMM_ERR_INVALID_ARG;
     return run_tile(h, mpg::PREC_W4A4, M, N, K / 2, A, lda / 2, B, ldb / 2, Y, ldy, stream, SX, SW, bias);
+}
+
+mpgemm_status_t mpgemm_run_w4a4_lowrank(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                        const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                                        const uint16_t *SX, const uint16_t *SW, const uint16_t *bias,
+                                        const uint16_t *X, int64_t ldx, const uint16_t *LD, int64_t ldd,
+                                        const uint16_t *LU, int64_t ldu, int64_t R,
+                                        uint16_t *Y, int64_t ldy, void *stream) {
+    if (R == 0)
+        return mpgemm_run_w4a4(h, M, N, K, A, lda, B, ldb, SX, SW, bias, Y, ldy, stream);
+    if (M > 0 && N > 0 && K >= 0 && ((K % 2) != 0 || (lda % 2) != 0 || (ldb % 2) != 0))
+        return MPGEMM_ERR_UNSUPPORTED;
+    bool noop;
+    mpgemm_status_t st =
+        check_gemm_args(M, N, K, A, lda, B, ldb, Y, ldy, 1, 2, 2, MPGEMM_MAX_K_INT, &noop);
+    if (st != MPGEMM_OK || noop)
+        return R < 0 ? MPGEMM_ERR_INVALID_ARG : st;
+    if (!SX || !SW || R < 0 || !LU || (K > 0 && (!X || !LD)) || ldx < K || ldd < K || ldu < R)
+        return MPGEMM_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(SX) | reinterpret_cast<uintptr_t>(SW) |
+         reinterpret_cast<uintptr_t>(bias) | reinterpret_cast<uintptr_t>(X) |
+         reinterpret_cast<uintptr_t>(LD)) & 1u)
+        return MPGEMM_ERR_UNSUPPORTED;
+    // the epilogue reads LU rows with 16-byte loads, 16 of rank per step
+    if (R % 16 != 0 || R > MPGEMM_MAX_LOWRANK || !aligned16(LU) || ldu % 8 != 0 ||
+        ldx > INT64_MAX / 4 || ldd > INT64_MAX / 4 || ldu > INT64_MAX / 4)
+        return MPGEMM_ERR_UNSUPPORTED;
+    if (!h)
+        return MPGEMM_ERR_INVALID_ARG;
+    // U = X LD^T (fp32, M x R) at the start of the handle's workspace; the
+    // stream-K partials of both launches get the rest
+    const int64_t ubytes = (M * R * 4 + 255) / 256 * 256;
+    if (ubytes > h->tile_ws.partial_bytes / 2)
+        return MPGEMM_ERR_UNSUPPORTED;
+    float *U = static_cast<float *>(h->tile_ws.partial);
+    mpg::TileWorkspace rest = h->tile_ws;
+    rest.partial = static_cast<uint8_t *>(h->tile_ws.partial) + ubytes;
+    rest.partial_bytes = h->tile_ws.partial_bytes - ubytes;
+    st = run_tile(h, mpg::PREC_F16, M, R, 2 * K, X, 2 * ldx, LD, 2 * ldd, U, R, stream, nullptr, nullptr,
+                  nullptr, nullptr, &rest);
+    if (st != MPGEMM_OK)
+        return st;
+    const LowRankArgs lr{U, LU, R, ldu, (int)R};
+    return run_tile(h, mpg::PREC_W4A4, M, N, K / 2, A, lda / 2, B, ldb / 2, Y, ldy, stream, SX, SW, bias,
+                    &lr, &rest);
 }
 
 mpgemm_status_t mpgemm_run_w4a16(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,

@@ -168,6 +168,34 @@ __device__ __forceinline__ void read_frags(const uint8_t *As, int step, int wm0,
     }
 }
 
+// The W4A4 low-rank term of one 32 x 32 output block (rows row_b ...
+// row_b + 31; this lane's column col): sum over r of fp16(U[m][r]) * V[n][r]
+// ("Warp-Specialized Kernel Implementation for W4A4 MatMul on Latest GPU
+// Architectures", section 1: the low-rank residual L(X) next to the 4-bit
+// product), on the matrix unit in the accumulator layout of the block, 16 of
+// rank per v_mfma_f32_32x32x16_f16. Lane l supplies row row_b + l % 32 of U
+// and column l % 32 of the block's V rows, ranks 8 (l / 32) ... + 7 of each
+// 16; U's fp32 values are rounded to fp16 (nearest even) on the way in. Rows
+// and columns past the problem are clamped (their outputs are not stored).
+__device__ __forceinline__ f32x16 lowrank_block(const GemmProblem &p, int row_b, int col) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const int lane = threadIdx.x & 63;
+    const int m = min(row_b + (lane & 31), p.M - 1);
+    const int n = min(col, p.N - 1);
+    const float *u = p.lr_u + (int64_t)m * p.lr_ldu + 8 * (lane >> 5);
+    const uint16_t *v = p.lr_v + (int64_t)n * p.lr_ldv + 8 * (lane >> 5);
+    f32x16 acc = {};
+    for (int t = 0; t < p.lr_rank; t += 16) {
+        const f32x4 u0 = *reinterpret_cast<const f32x4 *>(u + t);
+        const f32x4 u1 = *reinterpret_cast<const f32x4 *>(u + t + 4);
+        const f16x8 a = {(_Float16)u0[0], (_Float16)u0[1], (_Float16)u0[2], (_Float16)u0[3],
+                         (_Float16)u1[0], (_Float16)u1[1], (_Float16)u1[2], (_Float16)u1[3]};
+        const f16x8 b = *reinterpret_cast<const f16x8 *>(v + t);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
 // Epilogue. 32x32 accumulator layout: register r of lane l holds
 // row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the 32x32 block.
 template <int P, int TM, int TN>
@@ -183,6 +211,11 @@ __device__ __forceinline__ void store_tile(const GemmProblem &p, int row0, int c
         for (int j = 0; j < TN; ++j) {
             const int cl = j * 32 + (lane & 31);   // column within this wavefront's sub-tile
             const int col = col0 + cl;
+            f32x16 lr = {};
+            if constexpr (P == PREC_W4A4) {
+                if (p.lr_rank > 0)
+                    lr = lowrank_block(p, row0 + i * 32, col);
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rl = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
@@ -190,10 +223,11 @@ __device__ __forceinline__ void store_tile(const GemmProblem &p, int row0, int c
                 if (row < p.M && col < p.N) {
                     if constexpr (P == PREC_W4A4) {
                         // |acc >> 8| <= 64 K < 2^24: exact in fp32; then two
-                        // products and the bias in fp32, each rounded on its
-                        // own (no fused multiply-add), one rounding to fp16
+                        // products, the low-rank term (0 without one) and the
+                        // bias in fp32, each rounded on its own (no fused
+                        // multiply-add), one rounding to fp16
 #pragma clang fp contract(off)
-                        const float y = (float)(acc[i][j][r] >> 8) * fx[rl] * fw[cl] + fb[cl];
+                        const float y = ((float)(acc[i][j][r] >> 8) * fx[rl] * fw[cl] + lr[r]) + fb[cl];
                         C[(int64_t)row * p.ldc + col] = __builtin_bit_cast(uint16_t, (_Float16)y);
                     } else if constexpr (P == PREC_I4) {
                         C[(int64_t)row * p.ldc + col] = acc[i][j][r] >> 8;

@@ -28,6 +28,14 @@ struct GemmProblem {
     // 1 when C and every C row start on a 16-byte boundary (the tile epilogue
     // may then store four consecutive 4-byte outputs at once)
     int c_vec16;
+    // PREC_W4A4 low-rank branch, when lr_rank > 0 (a multiple of 16): the
+    // epilogue adds sum_r fp16(lr_u[m][r]) * lr_v[n][r] before the bias, with
+    // lr_u fp32 (M x lr_rank, row stride lr_ldu, 16-byte aligned rows) and
+    // lr_v fp16 bits (N x lr_rank, row stride lr_ldv, 16-byte aligned rows)
+    const float *lr_u = nullptr;
+    const uint16_t *lr_v = nullptr;
+    int64_t lr_ldu = 0, lr_ldv = 0;
+    int lr_rank = 0;
 };
 
 // Tile configurations of the square/rectangular tile kernel. The index is

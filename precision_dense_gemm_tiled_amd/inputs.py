@@ -173,3 +173,19 @@ def w4a4_problem(M: int, N: int, K: int, seed: int):
     SW = f16_uniform(seed, off + M, 1, N, 0.001, 0.01).reshape(N)
     bias = f16_weights(seed, off + M + N, 1, N, 0.1).reshape(N)
     return A, B, SX, SW, bias
+
+
+def w4a4_lowrank_problem(M: int, N: int, K: int, R: int, seed: int):
+    """The W4A4 problem of w4a4_problem plus the low-rank branch's inputs:
+    unquantised activations X (M x K fp16, N(0, 1)), down-projection LD
+    (R x K, 0.02 * N(0, 1)) and up-projection LU (N x R, 0.02 * N(0, 1)),
+    drawn from the same seed after the W4A4 inputs' draws (X is drawn on its
+    own, not the activations that A encodes)."""
+    A, B, SX, SW, bias = w4a4_problem(M, N, K, seed)
+    off = (M + N) * ((K + 1) // 2) + M + N + 2 * N
+    X = f16_normal(seed, off, M, K)
+    off += draws_f16_normal(M, K)
+    LD = f16_weights(seed, off, R, K)
+    off += 2 * R * K
+    LU = f16_weights(seed, off, N, R)
+    return A, B, SX, SW, bias, X, LD, LU

@@ -31,7 +31,7 @@ def test_header_declares_the_abi():
     names = declared_symbols()
     for n in ["mpgemm_create", "mpgemm_destroy", "mpgemm_status_string", "mpgemm_run_f16",
               "mpgemm_run_i8", "mpgemm_run_i4", "mpgemm_run_w4a16", "mpgemm_run_w4a4", "mpgemm_quantize_w4",
-              "mpgemm_run_f16_kn", "mpgemm_run_i8_kn", "mpgemm_run_i4_kn"]:
+              "mpgemm_run_w4a4_lowrank", "mpgemm_run_f16_kn", "mpgemm_run_i8_kn", "mpgemm_run_i4_kn"]:
         assert n in names
 
 
@@ -209,6 +209,41 @@ def test_quantize_argument_errors_without_device(mp, args, expect):
 ])
 def test_w4a4_argument_errors_without_device(mp, args, expect):
     assert mp.mpgemm_run_w4a4(None, *args, None) == expect
+
+
+# (M, N, K, A, lda, B, ldb, SX, SW, bias, X, ldx, LD, ldd, LU, ldu, R, Y, ldy)
+_LR = (4, 4, 32, A, 32, B, 32, S, S + 64, 0, A + 4096, 32, A + 8192, 32, A + 16384, 16, 16, C, 16)
+
+
+def _lr(**kw):
+    names = ["M", "N", "K", "A", "lda", "B", "ldb", "SX", "SW", "bias", "X", "ldx", "LD", "ldd", "LU", "ldu",
+             "R", "Y", "ldy"]
+    v = dict(zip(names, _LR))
+    v.update(kw)
+    return tuple(v[n] for n in names)
+
+
+@pytest.mark.parametrize("args,expect", [
+    (_lr(), 1),                                 # valid: NULL handle left
+    (_lr(R=0), 1),                              # R = 0 is the plain W4A4 call (NULL handle left)
+    (_lr(M=0), 0),                              # M = 0: no-op
+    (_lr(R=-16), 1),                            # negative rank
+    (_lr(R=24, ldu=24), 2),                     # rank not a multiple of 16
+    (_lr(R=272, ldu=272), 2),                   # rank above MPGEMM_MAX_LOWRANK
+    (_lr(LU=A + 16384 + 8), 2),                 # LU not 16-byte aligned
+    (_lr(ldu=20, R=16), 2),                     # LU row stride not a multiple of 8
+    (_lr(ldu=8), 1),                            # ldu < R
+    (_lr(ldx=16), 1),                           # ldx < K
+    (_lr(ldd=16), 1),                           # ldd < K
+    (_lr(X=0), 1),                              # no X
+    (_lr(LD=0), 1),                             # no down-projection
+    (_lr(LU=0), 1),                             # no up-projection
+    (_lr(X=A + 4097), 2),                       # X not 2-byte aligned
+    (_lr(K=31), 2),                             # odd K (the W4A4 rule)
+    (_lr(SX=0), 1),                             # no SX
+])
+def test_w4a4_lowrank_argument_errors_without_device(mp, args, expect):
+    assert mp.mpgemm_run_w4a4_lowrank(None, *args, None) == expect
 
 
 @pytest.mark.parametrize("args,expect", [
