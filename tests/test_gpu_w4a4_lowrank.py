@@ -60,8 +60,10 @@ def _check(A, B, K, sx, sw, b, X, LD, LU, got, what):
 
 @pytest.mark.parametrize("M,N,K,R,with_bias", [
     (1, 1, 2, 16, True), (64, 64, 128, 32, True), (300, 520, 200, 16, False), (33, 700, 130, 48, True),
-    (5, 17, 64, 128, True), (257, 129, 4096, 64, True), (1024, 1024, 1024, 256, True), (700, 300, 512, 32, False)])
+    (5, 17, 64, 128, True), (257, 129, 4096, 64, True), (1024, 1024, 1024, 256, True), (700, 300, 512, 32, False),
+    (40, 100, 256, 48, True), (3, 50, 4096, 80, False), (8192, 64, 1024, 32, True)])
 def test_lowrank_against_oracle(M, N, K, R, with_bias):
+    """Ragged shapes, ranks in partial 32-rank blocks, a tall skinny case."""
     A, B, sx, sw, b, X, LD, LU = inputs.w4a4_lowrank_problem(M, N, K, R, seed=M + 3 * N + K + R)
     b = b if with_bias else None
     got = _run(A, B, K, sx, sw, b, X, LD, LU)
