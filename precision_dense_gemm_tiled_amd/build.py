@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmpgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.cpp", "gemm_tile.hip", "w4a16.hip", "quantize.hip", "noalloc.hip", "stream_read.hip"]
+SOURCES = ["api.cpp", "gemm_tile.hip", "w4a16.hip", "quantize.hip", "noalloc.hip", "stream_read.hip", "lowrank.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

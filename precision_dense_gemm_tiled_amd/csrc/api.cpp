@@ -488,10 +488,22 @@ mpgemm_status_t mpgemm_run_w4a4_lowrank(mpgemm_handle_t h, int64_t M, int64_t N,
     mpg::TileWorkspace rest = h->tile_ws;
     rest.partial = static_cast<uint8_t *>(h->tile_ws.partial) + ubytes;
     rest.partial_bytes = h->tile_ws.partial_bytes - ubytes;
-    st = run_tile(h, mpg::PREC_F16, M, R, 2 * K, X, 2 * ldx, LD, 2 * ldd, U, R, stream, nullptr, nullptr,
-                  nullptr, nullptr, &rest);
-    if (st != MPGEMM_OK)
-        return st;
+    if (K > 0 && K % 64 == 0 && R <= 64 && aligned16(X) && aligned16(LD) && ldx % 8 == 0 && ldd % 8 == 0 &&
+        h->forced_tile_cfg < 0) {
+        // the skinny down-projection kernel (X read once, coalesced)
+        DeviceGuard dg(h->device);
+        if (!dg.ok)
+            return MPGEMM_ERR_HIP;
+        const mpg::LowRankDown d{X, LD, U, ldx, ldd, R, (int)M, (int)K, (int)R};
+        if (mpg::launch_lowrank_down(d, static_cast<hipStream_t>(stream)) != hipSuccess)
+            return MPGEMM_ERR_HIP;
+    } else {
+        // other layouts and ranks, or a forced tile configuration: the FP16 tile GEMM
+        st = run_tile(h, mpg::PREC_F16, M, R, 2 * K, X, 2 * ldx, LD, 2 * ldd, U, R, stream, nullptr, nullptr,
+                      nullptr, nullptr, &rest);
+        if (st != MPGEMM_OK)
+            return st;
+    }
     const LowRankArgs lr{U, LU, R, ldu, (int)R};
     return run_tile(h, mpg::PREC_W4A4, M, N, K / 2, A, lda / 2, B, ldb / 2, Y, ldy, stream, SX, SW, bias,
                     &lr, &rest);

@@ -168,32 +168,57 @@ __device__ __forceinline__ void read_frags(const uint8_t *As, int step, int wm0,
     }
 }
 
-// The W4A4 low-rank term of one 32 x 32 output block (rows row_b ...
-// row_b + 31; this lane's column col): sum over r of fp16(U[m][r]) * V[n][r]
-// ("Warp-Specialized Kernel Implementation for W4A4 MatMul on Latest GPU
-// Architectures", section 1: the low-rank residual L(X) next to the 4-bit
-// product), on the matrix unit in the accumulator layout of the block, 16 of
-// rank per v_mfma_f32_32x32x16_f16. Lane l supplies row row_b + l % 32 of U
-// and column l % 32 of the block's V rows, ranks 8 (l / 32) ... + 7 of each
-// 16; U's fp32 values are rounded to fp16 (nearest even) on the way in. Rows
-// and columns past the problem are clamped (their outputs are not stored).
-__device__ __forceinline__ f32x16 lowrank_block(const GemmProblem &p, int row_b, int col) {
+// The W4A4 low-rank term of one row of 32 x 32 output blocks (rows row_b ...
+// row_b + 31, columns col0 + 32 j + lane % 32 for the TN blocks j): sum over
+// r of fp16(U[m][r]) * V[n][r] ("Warp-Specialized Kernel Implementation for
+// W4A4 MatMul on Latest GPU Architectures", section 1: the low-rank residual
+// L(X) next to the 4-bit product), on the matrix unit in the accumulator
+// layout of the blocks, 16 of rank per v_mfma_f32_32x32x16_f16. Lane l
+// supplies row row_b + l % 32 of U (its fp32 values rounded to fp16, nearest
+// even, once per row of blocks) and column l % 32 of each block's V rows,
+// ranks 8 (l / 32) ... + 7 of each 16. Rows and columns past the problem are
+// clamped (their outputs are not stored).
+template <int TN>
+__device__ __forceinline__ void lowrank_row(const GemmProblem &p, int row_b, int col0, f32x16 (&lr)[TN]) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & 63;
     const int m = min(row_b + (lane & 31), p.M - 1);
-    const int n = min(col, p.N - 1);
     const float *u = p.lr_u + (int64_t)m * p.lr_ldu + 8 * (lane >> 5);
-    const uint16_t *v = p.lr_v + (int64_t)n * p.lr_ldv + 8 * (lane >> 5);
-    f32x16 acc = {};
-    for (int t = 0; t < p.lr_rank; t += 16) {
-        const f32x4 u0 = *reinterpret_cast<const f32x4 *>(u + t);
-        const f32x4 u1 = *reinterpret_cast<const f32x4 *>(u + t + 4);
-        const f16x8 a = {(_Float16)u0[0], (_Float16)u0[1], (_Float16)u0[2], (_Float16)u0[3],
-                         (_Float16)u1[0], (_Float16)u1[1], (_Float16)u1[2], (_Float16)u1[3]};
-        const f16x8 b = *reinterpret_cast<const f16x8 *>(v + t);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+    const uint16_t *v[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int n = min(col0 + 32 * j + (lane & 31), p.N - 1);
+        v[j] = p.lr_v + (int64_t)n * p.lr_ldv + 8 * (lane >> 5);
     }
-    return acc;
+    auto to_f16 = [](f32x4 x0, f32x4 x1) {
+        return f16x8{(_Float16)x0[0], (_Float16)x0[1], (_Float16)x0[2], (_Float16)x0[3],
+                     (_Float16)x1[0], (_Float16)x1[1], (_Float16)x1[2], (_Float16)x1[3]};
+    };
+    // 32 ranks per pass (the rank is a multiple of 16: the last pass may hold
+    // one step only, and then reads nothing past it)
+    for (int t = 0; t < p.lr_rank; t += 32) {
+        const bool two = t + 16 < p.lr_rank;
+        const f16x8 a0 = to_f16(*reinterpret_cast<const f32x4 *>(u + t), *reinterpret_cast<const f32x4 *>(u + t + 4));
+        f16x8 a1 = {};
+        f16x8 b0[TN], b1[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            b0[j] = *reinterpret_cast<const f16x8 *>(v[j] + t);
+        if (two) {
+            a1 = to_f16(*reinterpret_cast<const f32x4 *>(u + t + 16), *reinterpret_cast<const f32x4 *>(u + t + 20));
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                b1[j] = *reinterpret_cast<const f16x8 *>(v[j] + t + 16);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0[j], lr[j], 0, 0, 0);
+        if (two) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1[j], lr[j], 0, 0, 0);
+        }
+    }
 }
 
 // Epilogue. 32x32 accumulator layout: register r of lane l holds
@@ -206,16 +231,20 @@ __device__ __forceinline__ void store_tile(const GemmProblem &p, int row0, int c
     typedef typename AccOf<P>::out out_t;
     out_t *C = reinterpret_cast<out_t *>(p.C);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+        // the W4A4 low-rank term of this row of blocks (zero without one)
+        [[maybe_unused]] f32x16 lr[TN];
+        if constexpr (P == PREC_W4A4) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                lr[j] = f32x16{};
+            if (p.lr_rank > 0)
+                lowrank_row<TN>(p, row0 + i * 32, col0, lr);
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int cl = j * 32 + (lane & 31);   // column within this wavefront's sub-tile
             const int col = col0 + cl;
-            f32x16 lr = {};
-            if constexpr (P == PREC_W4A4) {
-                if (p.lr_rank > 0)
-                    lr = lowrank_block(p, row0 + i * 32, col);
-            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rl = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
@@ -227,7 +256,7 @@ __device__ __forceinline__ void store_tile(const GemmProblem &p, int row0, int c
                         // bias in fp32, each rounded on its own (no fused
                         // multiply-add), one rounding to fp16
 #pragma clang fp contract(off)
-                        const float y = ((float)(acc[i][j][r] >> 8) * fx[rl] * fw[cl] + lr[r]) + fb[cl];
+                        const float y = ((float)(acc[i][j][r] >> 8) * fx[rl] * fw[cl] + lr[j][r]) + fb[cl];
                         C[(int64_t)row * p.ldc + col] = __builtin_bit_cast(uint16_t, (_Float16)y);
                     } else if constexpr (P == PREC_I4) {
                         C[(int64_t)row * p.ldc + col] = acc[i][j][r] >> 8;
@@ -237,6 +266,7 @@ __device__ __forceinline__ void store_tile(const GemmProblem &p, int row0, int c
                 }
             }
         }
+    }
 }
 
 // Epilogue for transposed accumulators (mfma_step with TRANS): register r

@@ -202,4 +202,16 @@ struct QuantizeW4Problem {
 
 hipError_t launch_quantize_w4(const QuantizeW4Problem &p, hipStream_t stream);
 
+// Down-projection of the W4A4 low-rank branch, U = X LD^T: X (M x K fp16
+// bits, row stride ldx), LD (R x K, row stride ldd), U fp32 (M x R, row
+// stride ldu). Needs K % 64 == 0, 1 <= R <= 64, X and LD 16-byte aligned with
+// 16-byte aligned rows (the caller checks; other shapes take the tile GEMM).
+struct LowRankDown {
+    const uint16_t *X, *LD;
+    float *U;
+    int64_t ldx, ldd, ldu;
+    int M, K, R;
+};
+hipError_t launch_lowrank_down(const LowRankDown &p, hipStream_t stream);
+
 }  // namespace mpg
