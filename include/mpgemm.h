@@ -184,10 +184,12 @@ mpgemm_status_t mpgemm_run_w4a4(mpgemm_handle_t h, int64_t M, int64_t N, int64_t
  * with ldu a multiple of 8, X and LD 2-byte aligned (else
  * MPGEMM_ERR_UNSUPPORTED); R == 0 is mpgemm_run_w4a4. U lives in the
  * handle's workspace: M * R * 4 bytes (rounded up to 256) may take at most
- * half of it, else MPGEMM_ERR_UNSUPPORTED. Two launches on `stream`: U by the
- * FP16 tile kernel, then the W4A4 tile kernel, whose epilogue adds L per
- * 32 x 32 output block on the matrix unit. The fp32 sums' order is
- * unspecified; every other step rounds as written. */
+ * half of it, else MPGEMM_ERR_UNSUPPORTED. Two launches on `stream`: U (by a
+ * skinny down-projection kernel when R <= 64, K % 64 == 0 and X, LD have
+ * 16-byte aligned rows, else by the FP16 tile kernel), then the W4A4 tile
+ * kernel, whose epilogue adds L per 32 x 32 output block on the matrix unit.
+ * The fp32 sums' order is unspecified; every other step rounds as written;
+ * repeated calls give bit-identical results. */
 #define MPGEMM_MAX_LOWRANK 256
 mpgemm_status_t mpgemm_run_w4a4_lowrank(mpgemm_handle_t h, int64_t M, int64_t N, int64_t K,
                                         const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
