@@ -70,6 +70,22 @@ def test_lowrank_against_oracle(M, N, K, R, with_bias):
     _check(A, B, K, sx, sw, b, X, LD, LU, got, f"w4a4 low-rank {M}x{N}x{K} R={R}")
 
 
+def test_lowrank_random_shapes_reproducible():
+    """Twelve seeded random shapes (M, N up to 700, K a multiple of 2 up to
+    2048, R a multiple of 16 up to 128): against the oracle, and a second call
+    with the same inputs gives the same bits."""
+    r = np.random.default_rng(2026)
+    for i in range(12):
+        M, N = int(r.integers(1, 701)), int(r.integers(1, 701))
+        K = 2 * int(r.integers(1, 1025)) if i % 3 else 64 * int(r.integers(1, 33))
+        R = 16 * int(r.integers(1, 9))
+        A, B, sx, sw, b, X, LD, LU = inputs.w4a4_lowrank_problem(M, N, K, R, seed=300 + i)
+        got = _run(A, B, K, sx, sw, b, X, LD, LU)
+        _check(A, B, K, sx, sw, b, X, LD, LU, got, f"w4a4 low-rank {M}x{N}x{K} R={R}")
+        again = _run(A, B, K, sx, sw, b, X, LD, LU)
+        assert np.array_equal(got.view(np.uint16), again.view(np.uint16)), f"{M}x{N}x{K} R={R}: not reproducible"
+
+
 def test_lowrank_every_tile_config(monkeypatch):
     """Every tile configuration (forced for both launches: the FP16 down-
     projection and the W4A4 kernel with the low-rank epilogue); K = 512 also
