@@ -178,7 +178,7 @@ __device__ __forceinline__ void read_frags(const uint8_t *As, int step, int wm0,
 // even, once per row of blocks) and column l % 32 of each block's V rows,
 // ranks 8 (l / 32) ... + 7 of each 16. Rows and columns past the problem are
 // clamped (their outputs are not stored).
-template <int TN>
+template <int TN, bool TRANS = false>
 __device__ __forceinline__ void lowrank_row(const GemmProblem &p, int row_b, int col0, f32x16 (&lr)[TN]) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & 63;
@@ -210,13 +210,17 @@ __device__ __forceinline__ void lowrank_row(const GemmProblem &p, int row_b, int
             for (int j = 0; j < TN; ++j)
                 b1[j] = *reinterpret_cast<const f16x8 *>(v[j] + t + 16);
         }
+        // TRANS: operands swapped, so each block holds its transpose (the
+        // layout of the main loop's transposed accumulators)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0[j], lr[j], 0, 0, 0);
+            lr[j] = TRANS ? __builtin_amdgcn_mfma_f32_32x32x16_f16(b0[j], a0, lr[j], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0[j], lr[j], 0, 0, 0);
         if (two) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                lr[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1[j], lr[j], 0, 0, 0);
+                lr[j] = TRANS ? __builtin_amdgcn_mfma_f32_32x32x16_f16(b1[j], a1, lr[j], 0, 0, 0)
+                              : __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1[j], lr[j], 0, 0, 0);
         }
     }
 }
@@ -335,6 +339,83 @@ __device__ __forceinline__ void store_tile_lds(const GemmProblem &p, uint8_t *re
     }
 }
 
+// W4A4 epilogue for transposed accumulators (the layout store_tile_lds
+// reads: register r of lane l in block (i, j) holds row 32 i + l % 32 and
+// column 32 j + 8 (r / 4) + 4 (l / 32) + r % 4 of the wavefront's sub-tile).
+// Each output is computed in registers exactly as in store_tile:
+// fp16((((acc >> 8) * sx) * sw + low-rank term) + bias), each fp32 operation
+// rounded on its own; four consecutive columns are packed into 8 bytes and
+// staged RP rows at a time in the wavefront's own LDS region (row-major fp16,
+// 16-byte chunk c of row r at chunk c ^ (r % CPW)), then whole row segments
+// are read back and written with 16-byte stores (per-element stores at the
+// right edge, or when C rows are not 16-byte aligned). fx / fw / fb: the
+// staged row factors, column factors and bias of this sub-tile.
+template <int TM, int TN, int RP>
+__device__ __forceinline__ void store_tile_lds_w4a4(const GemmProblem &p, uint8_t *region, int row0, int col0,
+                                                    int lane, const i32x16 (&acc)[TM][TN], const float *fx,
+                                                    const float *fw, const float *fb) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int WTN = TN * 32, RB = WTN * 2, CPW = WTN / 8;   // bytes and 16-byte chunks per staged row
+    static_assert((CPW == 8 || CPW == 16) && RP % 32 == 0 && (TM * 32) % RP == 0 && (RP * CPW) % 64 == 0,
+                  "staging shape");
+    uint16_t *C = reinterpret_cast<uint16_t *>(p.C);
+    const bool vec = p.c_vec16 != 0 && p.ldc % 8 == 0;
+    const int h = lane >> 5;
+#pragma unroll
+    for (int pass = 0; pass < TM * 32 / RP; ++pass) {
+#pragma unroll
+        for (int ib = 0; ib < RP / 32; ++ib) {
+            const int i = pass * (RP / 32) + ib;
+            const int rl = ib * 32 + (lane & 31);
+            const float sx = fx[i * 32 + (lane & 31)];
+            f32x16 lr[TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                lr[j] = f32x16{};
+            if (p.lr_rank > 0)
+                lowrank_row<TN, true>(p, row0 + i * 32, col0, lr);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int cl = 32 * j + 8 * g + 4 * h;
+                    const f32x4 wv = *reinterpret_cast<const f32x4 *>(fw + cl);
+                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(fb + cl);
+                    u16x4 v;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+#pragma clang fp contract(off)
+                        const float y = ((float)(acc[i][j][4 * g + d] >> 8) * sx * wv[d] + lr[j][4 * g + d]) + bv[d];
+                        v[d] = __builtin_bit_cast(uint16_t, (_Float16)y);
+                    }
+                    const int c = 4 * j + g;
+                    *reinterpret_cast<u16x4 *>(region + rl * RB + ((c ^ (rl & (CPW - 1))) * 16) + 8 * h) = v;
+                }
+        }
+#pragma unroll
+        for (int q = 0; q < RP * CPW / 64; ++q) {
+            const int f = q * 64 + lane;
+            const int rl = f / CPW, c = f % CPW;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(region + rl * RB + ((c ^ (rl & (CPW - 1))) * 16));
+            const int row = row0 + pass * RP + rl, col = col0 + c * 8;
+            if (row < p.M) {
+                uint16_t *dst = C + (int64_t)row * p.ldc + col;
+                if (vec && col + 7 < p.N) {
+                    // non-temporal: Y is written once and never read back here
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
+                } else {
+#pragma unroll
+                    for (int d = 0; d < 8; ++d)
+                        if (col + d < p.N)
+                            dst[d] = (uint16_t)(v[d / 2] >> (16 * (d % 2)));
+                }
+            }
+        }
+    }
+}
+
 // W4A4 epilogue factors of a BM x BN tile staged in LDS as fp32 (the operand
 // buffers are free once every wavefront is past its last fragment read):
 // fac[0, BM) = SX of the tile's rows, fac[BM, BM + BN) = SW of its columns,
@@ -430,14 +511,18 @@ struct RingTile {
     // LDS budget, checked at build time (160 KiB per workgroup on gfx950).
     static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
     typedef typename AccOf<P>::type acc_t;
-    // Accumulators hold transposed blocks (operands swapped in the MFMA) for
-    // the 4-byte outputs, written back through LDS with 16-byte stores
-    // (store_tile_lds); the W4A4 epilogue keeps the direct layout.
-    static constexpr bool TRANS = P != PREC_W4A4 && WTN >= 64;
+    // Accumulators hold transposed blocks (operands swapped in the MFMA),
+    // written back through LDS with 16-byte stores (store_tile_lds; for W4A4
+    // store_tile_lds_w4a4, which stages fp16 outputs and keeps the tile's
+    // factor table at the end of the ring).
+    static constexpr bool TRANS = WTN >= 64;
     static constexpr int NW = WGM * WGN;
-    static constexpr int RP_MAX = (LDS_BYTES / NW) / (WTN * 4) / 32 * 32;   // rows one pass can stage
+    static constexpr int FACB = P == PREC_W4A4 ? ((BM + 2 * BN) * 4 + 15) / 16 * 16 : 0;   // factor table
+    static constexpr int OUTB = P == PREC_W4A4 ? 2 : 4;                                    // staged bytes per output
+    static constexpr int REGION = (LDS_BYTES - FACB) / NW / 16 * 16;                      // per wavefront
+    static constexpr int RP_MAX = REGION / (WTN * OUTB) / 32 * 32;   // rows one pass can stage
     static constexpr int RP = RP_MAX >= WTM ? WTM : (WTM % RP_MAX == 0 ? RP_MAX : 32);
-    static_assert(!TRANS || (RP >= 32 && RP * WTN * 4 * NW <= LDS_BYTES), "epilogue staging fits the ring");
+    static_assert(!TRANS || (RP >= 32 && RP * WTN * OUTB <= REGION), "epilogue staging fits the ring");
 
     // WEAVE: instruction order of one scheduling region of NMF MFMAs: the
     // TM + TN fragment reads two after each of the first MFMAs, then (step 0)
@@ -654,7 +739,14 @@ struct RingTile {
     static __device__ __forceinline__ void epilogue(const GemmProblem &p, uint8_t *smem, int row0,
                                                     int col0, int tid, int lane, int wave,
                                                     const acc_t (&acc)[TM][TN]) {
-        if constexpr (TRANS) {
+        if constexpr (TRANS && P == PREC_W4A4) {
+            const int wm0 = (wave / WGN) * WTM;
+            const int wn0 = (wave % WGN) * WTN;
+            float *fac = reinterpret_cast<float *>(smem + LDS_BYTES - FACB);
+            stage_factors<BM, BN, NT>(p, row0, col0, tid, fac);   // (barriers before and after)
+            store_tile_lds_w4a4<TM, TN, RP>(p, smem + wave * REGION, row0 + wm0, col0 + wn0, lane, acc,
+                                            fac + wm0, fac + BM + wn0, fac + BM + BN + wn0);
+        } else if constexpr (TRANS) {
             const int wm0 = (wave / WGN) * WTM;
             const int wn0 = (wave % WGN) * WTN;
             __syncthreads();
